@@ -1,0 +1,226 @@
+/*
+ * CPU oracle for the tiled f16/bf16 multiply-accumulate D = A * B^T + C.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the CPU
+ * baseline leg of the benchmark may load this library. The HIP product path
+ * neither links nor calls it, and this file shares no code, header, table or
+ * helper with that path.
+ *
+ * Plain, slow, obviously correct: every function is the definition from the
+ * pages written out as loops, with no blocking or reordering. Sources (Apache
+ * TVM "tirx" tile-op documentation):
+ *   - mma.sync page, "Operand coordinates and ownership" (shapes table): the
+ *     packed A (M_repeat, K_repeat, 16, k/2), B (N_repeat, K_repeat, 8, k/2)
+ *     and D / tensor C (M_repeat, N_repeat, 16, 8) float32 layouts; k = 16.
+ *   - mma.sync page, "Example: a 16x8 result with two K16 issues": the host
+ *     packing (reshape + transpose + view as uint32), hence the even K value
+ *     sits in the low 16 bits of a word on a little-endian host.
+ *   - mma.sync page, "Accumulation, transpose and alpha/beta": repeat order
+ *     batch, M, N, then K; C is a tensor or a scalar broadcast; only the first
+ *     K issue reads C, later issues read D.
+ *   - fma page, "Operand specification": a*b+c is a single rounding.
+ *   - cp.async.bulk.tensor page, "Operands and descriptor fields" and
+ *     "Example: two explicit 8x16 boxes": box / coords / coord_steps, the
+ *     compact (repeat, box...) image, out-of-bounds fill defaulting to zero.
+ *
+ * Readings where the pages leave a step open:
+ *   - within one hardware issue the summation order is not stated; the oracle
+ *     sums k in ascending order, one fp32 rounding per step (the accumulator
+ *     is float32 on the pages). Each product of two f16 (11-bit significand)
+ *     or two bf16 (8-bit) values is exact in fp32, so acc + a*b is one
+ *     rounding, the same as a fused multiply-add.
+ *   - a leading batch axis on A, B, C and D; batches are independent, and the
+ *     scalar C broadcasts over all of them.
+ *   - K_repeat = 0 leaves the empty sum: D = C.
+ *
+ * Pins (all in the CPU test suite): the page's own packing recipe and an
+ * arange closed form for the packer; round trip over all 65536 bit patterns;
+ * numpy/torch half decoders for h2f; int64 exact arithmetic for quarter-
+ * integer inputs (the page's worked example is one); float64 numpy matmul
+ * within the fp32 error bound for normal inputs; the page's two-box example
+ * for the box copy; brute-force padding for out-of-bounds boxes.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { ORACLE_F16 = 0, ORACLE_BF16 = 1 };
+
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ---- half-precision decode (IEEE-754 binary16; bfloat16 = top half of binary32) ---- */
+
+float oracle_h2f(uint16_t h, int dtype) {
+  if (dtype == ORACLE_BF16) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+  }
+  /* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+  int sign = (h >> 15) & 1;
+  int expo = (h >> 10) & 0x1f;
+  int frac = h & 0x3ff;
+  float v;
+  if (expo == 0)
+    v = ldexpf((float)frac, -24);                /* zero / subnormal: frac * 2^-24 */
+  else if (expo == 31)
+    v = frac ? NAN : INFINITY;
+  else
+    v = ldexpf((float)(frac + 1024), expo - 25); /* (1 + frac/1024) * 2^(expo-15) */
+  return sign ? -v : v;
+}
+
+void oracle_h2f_array(float* out, const uint16_t* in, int64_t n, int dtype) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_h2f(in[i], dtype);
+}
+
+/* ---- packing: row-major halves -> packed b32 atoms ----
+ * X is (batch, rows, K) with row stride ld (elements), batch stride rows*ld.
+ * P is (batch, rows/R, K/16, R, 8) words, R = 16 for A and 8 for B:
+ *   P[b, r, kr, i, w] = X[b, R*r+i, 16*kr+2*w] | X[b, R*r+i, 16*kr+2*w+1] << 16
+ */
+int oracle_pack(uint32_t* P, const uint16_t* X, int64_t batch, int64_t rows, int64_t K,
+                int64_t ld, int64_t R) {
+  if ((R != 16 && R != 8) || rows % R || K % 16 || ld < K) return -1;
+  const int64_t rows_rep = rows / R, K_rep = K / 16;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t r = 0; r < rows_rep; ++r)
+      for (int64_t kr = 0; kr < K_rep; ++kr)
+        for (int64_t i = 0; i < R; ++i)
+          for (int64_t w = 0; w < 8; ++w) {
+            const uint16_t* row = X + b * rows * ld + (R * r + i) * ld;
+            uint32_t lo = row[16 * kr + 2 * w];
+            uint32_t hi = row[16 * kr + 2 * w + 1];
+            P[(((b * rows_rep + r) * K_rep + kr) * R + i) * 8 + w] = lo | (hi << 16);
+          }
+  return 0;
+}
+
+/* Inverse of oracle_pack into a dense (batch, rows, K) array. */
+int oracle_unpack(uint16_t* X, const uint32_t* P, int64_t batch, int64_t rows, int64_t K,
+                  int64_t R) {
+  if ((R != 16 && R != 8) || rows % R || K % 16) return -1;
+  const int64_t rows_rep = rows / R, K_rep = K / 16;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t row = 0; row < rows; ++row)
+      for (int64_t k = 0; k < K; ++k) {
+        uint32_t word =
+            P[(((b * rows_rep + row / R) * K_rep + k / 16) * R + row % R) * 8 + (k % 16) / 2];
+        X[(b * rows + row) * K + k] = (uint16_t)((word >> (16 * (k % 2))) & 0xFFFFu);
+      }
+  return 0;
+}
+
+/* ---- multiply-accumulate ---- */
+
+/* Logical element (row, k) of a packed operand with atom height R. */
+static float packed_elem(const uint32_t* P, int64_t b, int64_t row, int64_t k, int64_t R,
+                         int64_t rows_rep, int64_t K_rep, int dtype) {
+  uint32_t word =
+      P[(((b * rows_rep + row / R) * K_rep + k / 16) * R + row % R) * 8 + (k % 16) / 2];
+  return oracle_h2f((uint16_t)((word >> (16 * (k % 2))) & 0xFFFFu), dtype);
+}
+
+/* Offset of logical output (m, n) in the (batch, M_repeat, N_repeat, 16, 8) layout. */
+static int64_t acc_offset(int64_t b, int64_t m, int64_t n, int64_t M_rep, int64_t N_rep) {
+  return (((b * M_rep + m / 16) * N_rep + n / 8) * 16 + m % 16) * 8 + n % 8;
+}
+
+/* One output element: acc starts at C (read once), then every k in order. */
+static float one_output(const uint32_t* A, const uint32_t* B, const float* C, float c,
+                        int64_t b, int64_t m, int64_t n, int64_t M_rep, int64_t N_rep,
+                        int64_t K_rep, int dtype) {
+  float acc = C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c;
+  for (int64_t k = 0; k < 16 * K_rep; ++k) {
+    float a = packed_elem(A, b, m, k, 16, M_rep, K_rep, dtype);
+    float x = packed_elem(B, b, n, k, 8, N_rep, K_rep, dtype);
+    acc = acc + a * x;
+  }
+  return acc;
+}
+
+/* D = A * B^T + C over the whole problem. C == NULL selects the scalar c. */
+int oracle_mma(float* D, const uint32_t* A, const uint32_t* B, const float* C, float c,
+               int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep, int dtype) {
+  if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+  const int64_t rows = batch * 16 * M_rep;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t bm = 0; bm < rows; ++bm) {
+    const int64_t b = bm / (16 * M_rep), m = bm % (16 * M_rep);
+    for (int64_t n = 0; n < 8 * N_rep; ++n)
+      D[acc_offset(b, m, n, M_rep, N_rep)] =
+          one_output(A, B, C, c, b, m, n, M_rep, N_rep, K_rep, dtype);
+  }
+  return 0;
+}
+
+/* Selected outputs only: idx holds count triples (b, m, n); out[i] gets D[b, m, n]. */
+int oracle_mma_sampled(float* out, const int64_t* idx, int64_t count, const uint32_t* A,
+                       const uint32_t* B, const float* C, float c, int64_t batch,
+                       int64_t M_rep, int64_t N_rep, int64_t K_rep, int dtype) {
+  if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+  for (int64_t i = 0; i < count; ++i) {
+    const int64_t *t = idx + 3 * i;
+    if (t[0] < 0 || t[0] >= batch || t[1] < 0 || t[1] >= 16 * M_rep || t[2] < 0 ||
+        t[2] >= 8 * N_rep)
+      return -1;
+  }
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t i = 0; i < count; ++i)
+    out[i] = one_output(A, B, C, c, idx[3 * i], idx[3 * i + 1], idx[3 * i + 2], M_rep, N_rep,
+                        K_rep, dtype);
+  return 0;
+}
+
+/* ---- box copy (global tensor region -> compact image) ----
+ * img[t, j_0, ..., j_{rank-1}] = G[coords + t*coord_step + j] when every
+ * coordinate lies inside dims, else zero (the default out-of-bounds fill).
+ * Strides are in bytes; the innermost stride equals the element size.
+ * Returns the image bytes written (n_repeat * prod(box) * elem_bytes), the
+ * quantity the page's example counts per barrier phase, or -1.
+ */
+int64_t oracle_box_copy(uint8_t* img, const uint8_t* G, int32_t rank, int32_t elem_bytes,
+                        const int64_t* dims, const int64_t* strides, const int32_t* box,
+                        const int64_t* coords, int32_t n_repeat, const int64_t* coord_step) {
+  if (rank < 1 || rank > 5 || n_repeat < 1) return -1;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return -1;
+  int64_t box_elems = 1;
+  for (int d = 0; d < rank; ++d) {
+    if (box[d] < 1 || box[d] > 256 || dims[d] < 1) return -1;
+    box_elems *= box[d];
+  }
+  if (strides[rank - 1] != elem_bytes) return -1;
+  for (int32_t t = 0; t < n_repeat; ++t) {
+    for (int64_t e = 0; e < box_elems; ++e) {
+      /* split e into box coordinates, innermost fastest */
+      int64_t j[5], rem = e;
+      for (int d = rank - 1; d >= 0; --d) {
+        j[d] = rem % box[d];
+        rem /= box[d];
+      }
+      int inside = 1;
+      int64_t off = 0;
+      for (int d = 0; d < rank; ++d) {
+        int64_t g = coords[d] + (int64_t)t * coord_step[d] + j[d];
+        if (g < 0 || g >= dims[d]) inside = 0;
+        off += g * strides[d];
+      }
+      uint8_t* out = img + ((int64_t)t * box_elems + e) * elem_bytes;
+      if (inside)
+        memcpy(out, G + off, (size_t)elem_bytes);
+      else
+        memset(out, 0, (size_t)elem_bytes);
+    }
+  }
+  return (int64_t)n_repeat * box_elems * elem_bytes;
+}

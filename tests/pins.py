@@ -1,0 +1,226 @@
+"""Pins for the CPU oracle: checks against what the pages and mathematics fix.
+
+Each pin takes an ``oracle.Oracle`` and raises AssertionError when the oracle
+disagrees. ``test_oracle.py`` runs them on the real oracle; ``test_oracle_
+mutations.py`` runs them on copies of the oracle with a planted mistake and
+requires that some pin fails, so that each pin is shown to bite.
+"""
+import numpy as np
+
+import workloads
+from tests import util
+
+
+def _quarter_bits(rng, shape, dtype):
+    return workloads.draw_operand(rng, "quarter", shape, dtype)
+
+
+def pin_h2f(o):
+    """The oracle's half decoder equals numpy (f16) and torch (bf16) on all
+    65536 bit patterns; NaN patterns decode to NaN."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    for dt in ("f16", "bf16"):
+        with np.errstate(invalid="ignore"):   # signalling-NaN patterns widen quietly
+            got = o.h2f(bits, dt).astype(np.float64)
+        ref = util.decode(bits, dt)
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan), dt
+        assert np.array_equal(got[~nan], ref[~nan]), dt
+
+
+def pin_pack_page_recipe(o):
+    """Packer == the page's reshape/transpose/view recipe (mma.sync page,
+    worked example host code), for several row and K atoms, both atom heights,
+    batch 2, and a row-padded source (ld > K)."""
+    rng = np.random.default_rng(1)
+    for R, rows, K in ((16, 48, 64), (8, 40, 96), (16, 16, 32)):
+        x = util.random_bits(rng, (2, rows, K))
+        assert np.array_equal(o.pack(x, R), util.page_recipe_pack(x, R)), (R, rows, K)
+        xp = util.random_bits(rng, (2, rows, K + 24))
+        assert np.array_equal(o.pack(xp, R, K=K), util.page_recipe_pack(xp[:, :, :K].copy(), R))
+    # the page's example: K = 32 packs to (M_repeat, K_repeat, 16, k/2) = (1, 2, 16, 8)
+    g = util.golden("mma_sync_worked_example.json")
+    P = o.pack(np.zeros((1, 16, 32), np.uint16), 16)
+    assert P.shape[1:] == (1, *g["packed_a_shape_uint32"][1:])
+    Q = o.pack(np.zeros((1, 8, 32), np.uint16), 8)
+    assert Q.shape[1:] == (1, *g["packed_b_shape_uint32"][1:])
+
+
+def pin_pack_arange(o):
+    """Closed form on arange input: word = x | (x+1) << 16 with
+    x = (R*r + i)*K + 16*kr + 2*w (the even K value in the low half)."""
+    for R, rows, K in ((16, 32, 48), (8, 24, 64)):
+        x = np.arange(rows * K, dtype=np.uint32).astype(np.uint16).reshape(1, rows, K)
+        P = o.pack(x, R)
+        r, kr, i, w = np.meshgrid(np.arange(rows // R), np.arange(K // 16), np.arange(R),
+                                  np.arange(8), indexing="ij")
+        xv = ((R * r + i) * K + 16 * kr + 2 * w).astype(np.uint32)
+        assert np.array_equal(P[0], xv | ((xv + 1) << 16)), (R, rows, K)
+
+
+def pin_roundtrip(o):
+    """unpack(pack(x)) == x on all 65536 bit patterns (NaN encodings included),
+    for both atom heights: the packer moves bits, never values."""
+    x = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(1, 256, 256)
+    for R in (16, 8):
+        assert np.array_equal(o.unpack(o.pack(x, R), R), x), R
+
+
+def pin_page_example(o):
+    """The worked 16x8 example: the page's recipe, two K16 issues, scalar C=0,
+    gives exactly a.f32 @ b.f32.T (the products and sums are exact), which also
+    meets the page's rtol=atol=2e-4 check."""
+    g = util.golden("mma_sync_worked_example.json")
+    r = g["recipe"]
+    rng = np.random.default_rng(r["seed"])
+    a = (rng.integers(r["integers_low"], r["integers_high_exclusive"], r["a_shape"])
+         / r["divide_by"]).astype(r["dtype"])
+    b = (rng.integers(r["integers_low"], r["integers_high_exclusive"], r["b_shape"])
+         / r["divide_by"]).astype(r["dtype"])
+    ap, bp = o.pack(a.view(np.uint16), 16), o.pack(b.view(np.uint16), 8)
+    assert ap.reshape(g["packed_a_shape_uint32"]).shape == tuple(g["packed_a_shape_uint32"])
+    assert ap.shape[2] == g["K_repeat"] and bp.shape[1] == g["N_repeat"]
+    D = o.mma(ap, bp, None, g["scalar_c"], "f16")
+    out = util.tile_to_logical(D)[0]
+    assert out.shape == tuple(g["out_shape_float32"])
+    ref = a.astype(np.float32) @ b.astype(np.float32).T
+    np.testing.assert_allclose(out, ref, **g["page_tolerance"])
+    assert np.array_equal(out, ref)
+    exact16 = (4 * a.astype(np.float64)).astype(np.int64) @ \
+        (4 * b.astype(np.float64)).astype(np.int64).T
+    assert np.array_equal((out * 16).astype(np.int64), exact16)
+
+
+def pin_quarter_closed_form(o):
+    """Quarter-integer inputs: 16*D = 16*C + sum_k (4a)(4b) in int64 exactly,
+    for both dtypes, batch 2, odd repeat counts, tensor and scalar C."""
+    rng = np.random.default_rng(2)
+    for dt, (batch, Mr, Nr, Kr) in (("f16", (2, 3, 5, 7)), ("bf16", (2, 2, 3, 4)),
+                                    ("bf16", (1, 1, 1, 1))):
+        M, N, K = 16 * Mr, 8 * Nr, 16 * Kr
+        a = _quarter_bits(rng, (batch, M, K), dt)
+        b = _quarter_bits(rng, (batch, N, K), dt)
+        c_int = rng.integers(-64, 65, (batch, M, N))
+        C = util.logical_to_tile((c_int / 4).astype(np.float32))
+        ai = (4 * util.decode(a, dt)).astype(np.int64)
+        bi = (4 * util.decode(b, dt)).astype(np.int64)
+        prod = np.einsum("bmk,bnk->bmn", ai, bi)
+        A, B = o.pack(a, 16), o.pack(b, 8)
+        D = util.tile_to_logical(o.mma(A, B, C, 0.0, dt))
+        assert np.array_equal((D * 16).astype(np.int64), 4 * c_int + prod), (dt, batch, Mr, Nr, Kr)
+        D2 = util.tile_to_logical(o.mma(A, B, None, -1.25, dt))
+        assert np.array_equal((D2 * 16).astype(np.int64), prod - 20), (dt, "scalar")
+
+
+def pin_normal_vs_float64(o):
+    """Normal inputs: |D - D_f64| <= gamma_K * (|A||B|^T + |C|) elementwise,
+    the worst-case bound of K sequential fp32 additions, against float64 numpy
+    matmul of the same half values."""
+    rng = np.random.default_rng(3)
+    for dt, (batch, Mr, Nr, Kr) in (("bf16", (2, 2, 3, 37)), ("f16", (1, 3, 2, 21))):
+        M, N, K = 16 * Mr, 8 * Nr, 16 * Kr
+        a = workloads.draw_operand(rng, "normal", (batch, M, K), dt)
+        b = workloads.draw_operand(rng, "normal", (batch, N, K), dt)
+        C = rng.standard_normal((batch, Mr, Nr, 16, 8), dtype=np.float32)
+        A, B = o.pack(a, 16), o.pack(b, 8)
+        D = util.tile_to_logical(o.mma(A, B, C, 0.0, dt)).astype(np.float64)
+        af, bf = util.decode(a, dt), util.decode(b, dt)
+        Cl = util.tile_to_logical(C).astype(np.float64)
+        ref = af @ bf.transpose(0, 2, 1) + Cl
+        mag = np.abs(af) @ np.abs(bf).transpose(0, 2, 1) + np.abs(Cl)
+        err = np.abs(D - ref)
+        assert (err <= util.gamma(K) * mag).all(), (dt, float((err / mag).max()))
+        # and the rounding is real: the fp32 result is not the fp64 sum cast once
+        assert not np.array_equal(D, ref.astype(np.float32).astype(np.float64))
+
+
+def pin_recurrence_chain(o):
+    """C-then-D recurrence: one call over K equals calls chained over K chunks
+    (C -> D -> D ...), bitwise, on normal data and with a scalar start."""
+    rng = np.random.default_rng(4)
+    dt, batch, Mr, Nr, Kr = "bf16", 1, 2, 3, 9
+    M, N, K = 16 * Mr, 8 * Nr, 16 * Kr
+    a = workloads.draw_operand(rng, "normal", (batch, M, K), dt)
+    b = workloads.draw_operand(rng, "normal", (batch, N, K), dt)
+    C = rng.standard_normal((batch, Mr, Nr, 16, 8), dtype=np.float32)
+    A, B = o.pack(a, 16), o.pack(b, 8)
+    full = o.mma(A, B, C, 0.0, dt)
+    for cuts in ((4,), (1, 5), (2, 3, 7)):
+        bounds = [0, *cuts, Kr]
+        D = C
+        for lo, hi in zip(bounds[:-1], bounds[1:]):
+            D = o.mma(A[:, :, lo:hi], B[:, :, lo:hi], D, 0.0, dt)
+        assert np.array_equal(D, full), cuts
+    full_s = o.mma(A, B, None, 0.5, dt)
+    D = o.mma(A[:, :, :3], B[:, :, :3], None, 0.5, dt)
+    D = o.mma(A[:, :, 3:], B[:, :, 3:], D, 0.0, dt)
+    assert np.array_equal(D, full_s)
+
+
+def pin_zero_a_and_scalar(o):
+    """A = 0 gives D == C bitwise; a scalar c gives the same bits as a C tensor
+    filled with c; K_repeat = 0 (empty sum) gives D == C."""
+    rng = np.random.default_rng(5)
+    dt, batch, Mr, Nr, Kr = "f16", 2, 2, 3, 4
+    M, N, K = 16 * Mr, 8 * Nr, 16 * Kr
+    b = workloads.draw_operand(rng, "normal", (batch, N, K), dt)
+    C = rng.standard_normal((batch, Mr, Nr, 16, 8), dtype=np.float32)
+    A0 = o.pack(np.zeros((batch, M, K), np.uint16), 16)
+    B = o.pack(b, 8)
+    assert np.array_equal(o.mma(A0, B, C, 0.0, dt), C)
+    a = workloads.draw_operand(rng, "normal", (batch, M, K), dt)
+    A = o.pack(a, 16)
+    c = np.float32(0.7)
+    assert np.array_equal(o.mma(A, B, None, c, dt), o.mma(A, B, np.full_like(C, c), 0.0, dt))
+    assert np.array_equal(o.mma(A[:, :, :0], B[:, :, :0], C, 0.0, dt), C)
+
+
+def pin_sampled_matches_full(o):
+    """The sampled entry point returns exactly the full result's elements."""
+    rng = np.random.default_rng(6)
+    dt, batch, Mr, Nr, Kr = "bf16", 2, 3, 5, 6
+    M, N, K = 16 * Mr, 8 * Nr, 16 * Kr
+    A = o.pack(workloads.draw_operand(rng, "normal", (batch, M, K), dt), 16)
+    B = o.pack(workloads.draw_operand(rng, "normal", (batch, N, K), dt), 8)
+    C = rng.standard_normal((batch, Mr, Nr, 16, 8), dtype=np.float32)
+    full = util.tile_to_logical(o.mma(A, B, C, 0.0, dt))
+    idx = util.sample_indices(rng, batch, M, N, 200)
+    got = o.mma_sampled(A, B, C, 0.0, dt, idx)
+    assert np.array_equal(got, full[idx[:, 0], idx[:, 1], idx[:, 2]])
+
+
+def pin_box_page_example(o):
+    """The page's two-box example: the (2,8,16) image read back row by row is
+    arange(256); 512 bytes per box, 1024 per barrier phase."""
+    g = util.golden("tma_two_box_example.json")
+    x = np.arange(256, dtype=np.uint32).reshape(16, 16)
+    img, nbytes = o.box_copy(x, g["box"], g["coords"], g["n_repeat"], g["coord_steps"][0])
+    assert img.shape == tuple(g["image_shape"])
+    assert nbytes == g["bytes_per_barrier_phase"] == g["n_repeat"] * g["bytes_per_box"]
+    assert np.array_equal(img.reshape(16, 16), x)
+
+
+def pin_box_oob(o):
+    """Boxes partly outside the tensor: inside elements are copied, the rest
+    are zero (the default fill); checked against zero-padding + slicing, for
+    ranks 1-3, several element sizes, negative starts and repeat steps."""
+    rng = np.random.default_rng(7)
+    cases = [
+        (np.uint32, (16, 16), (8, 16), (-3, 5), 3, (6, -4)),
+        (np.uint16, (5, 7, 9), (4, 4, 8), (3, -2, 4), 2, (-4, 3, 1)),
+        (np.uint8, (37,), (32,), (20,), 2, (-25,)),
+        (np.uint64, (9, 11), (3, 5), (0, 0), 4, (3, 3)),
+    ]
+    for dtype, shape, box, coords, rep, step in cases:
+        x = rng.integers(1, 200, shape).astype(dtype)
+        img, nbytes = o.box_copy(x, box, coords, rep, step)
+        pad = 300
+        xp = np.pad(x, [(pad, pad)] * len(shape))
+        for t in range(rep):
+            start = [pad + c + t * s for c, s in zip(coords, step)]
+            ref = xp[tuple(slice(s0, s0 + bx) for s0, bx in zip(start, box))]
+            assert np.array_equal(img[t], ref), (dtype, shape, t)
+        assert nbytes == rep * int(np.prod(box)) * np.dtype(dtype).itemsize
+
+
+ALL_PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}

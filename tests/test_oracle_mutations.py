@@ -1,0 +1,72 @@
+"""Each pin bites: copies of the oracle with one planted mistake (a dropped
+term, a wrong index, swapped halves, a transposed layout, a wrong rounding
+point) must fail the pins named for it. Runs on the CPU only."""
+import os
+
+import pytest
+
+import oracle
+from tests import pins
+
+MUTATIONS = {
+    "pack_halves_swapped": (
+        "= lo | (hi << 16);", "= hi | (lo << 16);",
+        ["pin_pack_page_recipe", "pin_pack_arange"]),
+    "pack_rows_and_k_atoms_transposed": (
+        "P[(((b * rows_rep + r) * K_rep + kr) * R + i) * 8 + w]",
+        "P[(((b * rows_rep + r) * R + i) * K_rep + kr) * 8 + w]",
+        ["pin_pack_page_recipe", "pin_pack_arange"]),
+    "f16_exponent_bias_off_by_one": (
+        "expo - 25)", "expo - 24)",
+        ["pin_h2f", "pin_page_example", "pin_quarter_closed_form"]),
+    "f16_subnormal_scale_wrong": (
+        "ldexpf((float)frac, -24)", "ldexpf((float)frac, -25)", ["pin_h2f"]),
+    "operand_rows_reversed_in_atom": (
+        "* R + row % R) * 8 + (k % 16) / 2];\n  return oracle_h2f",
+        "* R + (R - 1 - row % R)) * 8 + (k % 16) / 2];\n  return oracle_h2f",
+        ["pin_page_example", "pin_quarter_closed_form", "pin_normal_vs_float64"]),
+    "c_added_at_every_k16_issue": (
+        "acc = acc + a * x;",
+        "acc = acc + a * x;\n    if (k % 16 == 15 && k + 1 < 16 * K_rep)"
+        " acc = acc + (C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c);",
+        ["pin_quarter_closed_form", "pin_recurrence_chain", "pin_zero_a_and_scalar"]),
+    "c_ignored": (
+        "float acc = C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c;", "float acc = 0.0f;",
+        ["pin_quarter_closed_form", "pin_zero_a_and_scalar", "pin_recurrence_chain"]),
+    "accumulator_in_double": (
+        "float acc = C ? C[", "double acc = C ? C[",
+        ["pin_normal_vs_float64", "pin_recurrence_chain"]),
+    "output_atom_transposed": (
+        "* N_rep + n / 8) * 16 + m % 16) * 8 + n % 8;",
+        "* N_rep + n / 8) * 8 + n % 8) * 16 + m % 16;",
+        ["pin_page_example", "pin_quarter_closed_form"]),
+    "last_k_atom_dropped": (
+        "k < 16 * K_rep; ++k) {\n    float a", "k < 16 * K_rep - 16; ++k) {\n    float a",
+        ["pin_page_example", "pin_quarter_closed_form"]),
+    "box_fill_not_zero": (
+        "memset(out, 0, (size_t)elem_bytes);", "memset(out, 0x5a, (size_t)elem_bytes);",
+        ["pin_box_oob"]),
+    "box_repeat_step_ignored": (
+        "coords[d] + (int64_t)t * coord_step[d] + j[d]", "coords[d] + j[d]",
+        ["pin_box_page_example", "pin_box_oob"]),
+    "box_image_repeat_innermost": (
+        "img + ((int64_t)t * box_elems + e) * elem_bytes",
+        "img + (e * n_repeat + t) * elem_bytes",
+        ["pin_box_page_example", "pin_box_oob"]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, tmp_path):
+    old, new, expected = MUTATIONS[name]
+    src = oracle.source_text()
+    assert src.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
+    path = oracle.build_variant(src.replace(old, new), os.path.join(tmp_path, f"lib_{name}.so"))
+    o = oracle.Oracle(path)
+    failed = []
+    for pin in expected:
+        try:
+            pins.ALL_PINS[pin](o)
+        except (AssertionError, ValueError):
+            failed.append(pin)
+    assert failed == expected, f"{name}: only {failed} of {expected} caught it"

@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs for the tiled f16/bf16 multiply-accumulate.
+
+This module only draws numbers and lays them out; it holds none of the
+method's arithmetic (no packing, no products, no sums), so both the CPU
+oracle and the HIP path can take their inputs from it without sharing any
+computation.
+
+Recipes (all from ``numpy.random.default_rng(seed)``, draws in the order A,
+B, C):
+
+* ``quarter``: integers uniform in [-4, 4] divided by 4, stored as f16 (the
+  recipe of the worked 16x8 example on the mma.sync page, "Example: a 16x8
+  result with two K16 issues"). These values are exact in f16 and bf16.
+* ``normal``: ``standard_normal(float32) * scale``, rounded once to bf16 with
+  round-to-nearest-even (or to f16 with numpy's own round-to-nearest-even).
+* C, when it is a tensor, is standard normal float32 drawn directly in the
+  atom-tiled accumulator layout (batch, M/16, N/8, 16, 8); the draws are
+  i.i.d., so drawing in the stored layout changes no statistics.
+
+Half-precision operands are returned as uint16 bit patterns, row-major
+(batch, rows, K).
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+F16, BF16 = "f16", "bf16"
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round-to-nearest-even); return uint16 bits.
+
+    Input quantisation only: NaN is not expected in the synthetic draws and is
+    rejected.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if np.isnan(x).any():
+        raise ValueError("NaN in bf16 quantisation input")
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    M: int
+    N: int
+    K: int
+    dtype: str            # "f16" | "bf16"
+    a_dist: str           # "quarter" | "normal"
+    b_dist: str
+    b_scale: float = 1.0
+    c_tensor: bool = False
+    c_scalar: float = 0.0
+    exact: bool = False   # every product and partial sum is exact in fp32
+
+    @property
+    def M_rep(self) -> int:
+        return self.M // 16
+
+    @property
+    def N_rep(self) -> int:
+        return self.N // 8
+
+    @property
+    def K_rep(self) -> int:
+        return self.K // 16
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.batch * self.M * self.N * self.K
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        """Compulsory HBM bytes of one multiply-accumulate call: packed A and
+        B read once, C read once if it is a tensor, D written once."""
+        a = self.batch * self.M * self.K * 2
+        b = self.batch * self.N * self.K * 2
+        d = self.batch * self.M * self.N * 4
+        return a + b + d + (d if self.c_tensor else 0)
+
+
+WORKLOADS = {
+    w.name: w
+    for w in [
+        # The worked example: M_repeat = N_repeat = 1, K_repeat = 2, scalar C = 0.
+        Workload("tile_16x8x32_f16", 1, 16, 8, 32, F16, "quarter", "quarter", exact=True),
+        Workload("gemm_128x128x256_bf16_ctensor", 1, 128, 128, 256, BF16, "normal", "normal",
+                 c_tensor=True),
+        Workload("gemm_4096_f16_quarter", 1, 4096, 4096, 4096, F16, "quarter", "quarter",
+                 exact=True),
+        Workload("skinny_16x16384x16384_bf16", 1, 16, 16384, 16384, BF16, "normal", "normal",
+                 b_scale=0.02),
+        Workload("gemm_8192_bf16_ctensor", 1, 8192, 8192, 8192, BF16, "normal", "normal",
+                 c_tensor=True),
+    ]
+}
+
+# The headline compute-bound workload that bench.py times.
+HEADLINE = "gemm_8192_bf16_ctensor"
+SKINNY = "skinny_16x16384x16384_bf16"
+
+
+def draw_operand(rng: np.random.Generator, dist: str, shape, dtype: str, scale: float = 1.0):
+    if dist == "quarter":
+        vals = rng.integers(-4, 5, shape) / 4
+        if dtype == F16:
+            return vals.astype(np.float16).view(np.uint16)
+        return f32_to_bf16_bits(vals.astype(np.float32))
+    if dist == "normal":
+        x = rng.standard_normal(shape, dtype=np.float32)
+        if scale != 1.0:
+            x = x * np.float32(scale)
+        return f32_to_bf16_bits(x) if dtype == BF16 else f32_to_f16_bits(x)
+    raise ValueError(f"unknown distribution {dist!r}")
+
+
+def make_inputs(w: Workload, seed: int = 0, a_dist: str | None = None,
+                b_dist: str | None = None):
+    """Return dict(a, b, c_tensor, c_scalar) for workload ``w``.
+
+    ``a``/``b`` are uint16 (batch, M, K) / (batch, N, K) row-major bits; the
+    optional distribution overrides build quantised variants of a shape.
+    """
+    rng = np.random.default_rng(seed)
+    a = draw_operand(rng, a_dist or w.a_dist, (w.batch, w.M, w.K), w.dtype)
+    b = draw_operand(rng, b_dist or w.b_dist, (w.batch, w.N, w.K), w.dtype, w.b_scale)
+    c = None
+    if w.c_tensor:
+        c = rng.standard_normal((w.batch, w.M_rep, w.N_rep, 16, 8), dtype=np.float32)
+    return dict(a=a, b=b, c_tensor=c, c_scalar=np.float32(w.c_scalar))
+
+
+def custom(batch, M, N, K, dtype=BF16, a_dist="normal", b_dist="normal", c_tensor=False,
+           c_scalar=0.0, b_scale=1.0, name="custom") -> Workload:
+    return Workload(name, batch, M, N, K, dtype, a_dist, b_dist, b_scale, c_tensor, c_scalar,
+                    exact=(a_dist == "quarter" and b_dist == "quarter"))
