@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Throughput of the packed f16/bf16 multiply-accumulate D = A * B^T + C on
+one MI355X.
+
+One step is the whole path over one batch of synthetic input already resident
+in HBM: pack A (row-major halves -> packed words), pack B, and the
+multiply-accumulate from C into D. Prints ONE JSON line on stdout.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--kernel auto]
+
+``value`` is 2*M*N*K*batch / (time per step) in TFLOP/s. ``roofline`` is for
+the step's dominant kernel, timed with HIP events on the stream it runs on;
+``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
+workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+METRIC = "TFLOP/s for f16/bf16 A·Bᵀ+C (fp32 acc) and % of MFMA/HBM roofline"
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense, published
+PEAK_HBM_GBS = 8000.0                                  # MI355X HBM3E, published
+RIDGE_FLOP_PER_BYTE = 2500e12 / 8000e9
+KERNEL_SOURCES = {
+    "mma_tile": ["mma_direct.hip", "mma_tiled.hip", "mma_skinny.hip", "common.h"],
+    "pack_operand": ["pack.hip", "common.h"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(kernel: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        p = os.path.join(ROOT, "bf16_matrix_multiply_amd", "csrc", f)
+        if os.path.exists(p):
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since it was taken."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("source_sha") != source_sha(kernel):
+        log(f"traffic record {p} is stale (kernel source changed); reporting null")
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, inp, D_gpu, seconds: float):
+    """The oracle, as it stands, on the first rows of D (all N columns), sized
+    to take about ``seconds`` of CPU time; also checks those rows against the
+    GPU result."""
+    import oracle
+    from_rows = w.batch == 1
+    A = oracle.pack(inp["a"], 16)
+    B = oracle.pack(inp["b"], 8)
+    C = inp["c_tensor"]
+
+    def run(rows):
+        idx = np.stack([np.zeros(rows * w.N, np.int64),
+                        np.repeat(np.arange(rows, dtype=np.int64), w.N),
+                        np.tile(np.arange(w.N, dtype=np.int64), rows)], axis=1)
+        t0 = time.perf_counter()
+        out = oracle.mma_sampled(A, B, C, inp["c_scalar"], w.dtype, idx)
+        return time.perf_counter() - t0, out, idx
+
+    probe_rows = min(w.M, 4)
+    t_probe, _, _ = run(probe_rows)
+    rows = int(max(probe_rows, min(w.M, seconds / max(t_probe, 1e-6) * probe_rows)))
+    t, out, idx = run(rows)
+    flops = 2.0 * rows * w.N * w.K
+    Dl = D_gpu.transpose(0, 1, 3, 2, 4).reshape(w.batch, w.M, w.N)
+    got = Dl[idx[:, 0], idx[:, 1], idx[:, 2]]
+    if w.exact:
+        ok = bool(np.array_equal(got, out))
+    else:
+        bnd = oracle.bound(A, B, C, inp["c_scalar"], w.dtype, idx)
+        ok = bool((np.abs(got.astype(np.float64) - out) <= 1e-3 * bnd).all())
+    assert from_rows
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle", "seconds": round(t, 3),
+            "sample": f"first {rows} rows of D x all {w.N} columns ({rows * w.N} outputs, "
+                      f"K={w.K} each) of workload {w.name}",
+            "sample_matches_gpu": ok}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--kernel", default="auto", choices=["auto", "direct", "tiled", "skinny"])
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("bench.py measures one GPU only: this path has no multi-GPU leg "
+               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).")
+        log(msg)
+        print(json.dumps({"error": msg, "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import bf16_matrix_multiply_amd as bmm
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.WORKLOADS[args.workload]
+    log(f"[bench] workload {w.name}: batch={w.batch} M={w.M} N={w.N} K={w.K} {w.dtype} "
+        f"C={'tensor' if w.c_tensor else 'scalar'}")
+    inp = workloads.make_inputs(w, seed=0)
+    a = torch.from_numpy(inp["a"].view(np.int16)).to(dev)
+    b = torch.from_numpy(inp["b"].view(np.int16)).to(dev)
+    C = None if inp["c_tensor"] is None else torch.from_numpy(inp["c_tensor"]).to(dev)
+    c = float(inp["c_scalar"])
+    A = torch.empty((w.batch, w.M_rep, w.K_rep, 16, 8), dtype=torch.int32, device=dev)
+    B = torch.empty((w.batch, w.N_rep, w.K_rep, 8, 8), dtype=torch.int32, device=dev)
+    D = torch.empty((w.batch, w.M_rep, w.N_rep, 16, 8), dtype=torch.float32, device=dev)
+    kernel = bmm.select_kernel(w.batch, w.M_rep, w.N_rep, w.K_rep) if args.kernel == "auto" \
+        else args.kernel
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        bmm.pack_operand(a, 16, out=A)
+        if ev is not None:
+            ev[1].record(stream)
+        bmm.pack_operand(b, 8, out=B)
+        if ev is not None:
+            ev[2].record(stream)
+        bmm.mma_tile(A, B, C, c, w.dtype, out=D, kernel=kernel)
+        if ev is not None:
+            ev[3].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    pa = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    pb = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    mm = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    log(f"[bench] {args.steps} steps: {total_ms:.3f} ms on events, {wall_ms:.3f} ms wall; "
+        f"pack A {pa.mean()*1e3:.1f} us, pack B {pb.mean()*1e3:.1f} us, "
+        f"mma_tile[{kernel}] {mm.mean()*1e3:.1f} us (min {mm.min()*1e3:.1f})")
+
+    value = w.flops / (ms_per_step * 1e-3) / 1e12
+    op_bytes = 2 * (w.batch * w.M * w.K * 2)          # pack A: read + write
+    op_bytes_b = 2 * (w.batch * w.N * w.K * 2)        # pack B: read + write
+    mma_s = mm.mean() * 1e-3
+    intensity = w.flops / w.algorithmic_bytes
+    times = {"mma_tile": mm.mean(), "pack_operand": pa.mean() + pb.mean()}
+    dominant = max(times, key=times.get)
+    if dominant == "mma_tile":
+        if intensity >= RIDGE_FLOP_PER_BYTE:
+            achieved, peak, unit, bound = w.flops / mma_s / 1e12, PEAK_MFMA_TFLOPS[w.dtype], \
+                "TFLOP/s", "mfma"
+        else:
+            achieved, peak, unit, bound = w.algorithmic_bytes / mma_s / 1e9, PEAK_HBM_GBS, \
+                "GB/s", "hbm"
+    else:
+        pack_s = (pa.mean() + pb.mean()) * 1e-3
+        achieved, peak, unit, bound = (op_bytes + op_bytes_b) / pack_s / 1e9, PEAK_HBM_GBS, \
+            "GB/s", "hbm"
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4),
+                "traffic": traffic_from_profiles(dominant, w.name),
+                "kernel": dominant if dominant != "mma_tile" else f"mma_tile[{kernel}]",
+                "avg_launch_us": round(times[dominant] * 1e3, 2),
+                "algorithmic_bytes_per_launch": w.algorithmic_bytes if dominant == "mma_tile"
+                else op_bytes + op_bytes_b}
+
+    line = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
+                   "c": "tensor" if w.c_tensor else "scalar", "kernel": kernel,
+                   "step": "pack A + pack B + mma_tile"},
+        "roofline": roofline,
+        "kernels": {"pack_a_us": round(pa.mean() * 1e3, 2), "pack_b_us": round(pb.mean() * 1e3, 2),
+                    "mma_tile_us": round(mm.mean() * 1e3, 2),
+                    "mma_tile_tflops": round(w.flops / mma_s / 1e12, 2),
+                    "mma_tile_gbs": round(w.algorithmic_bytes / mma_s / 1e9, 1),
+                    "pack_gbs": round((op_bytes + op_bytes_b) / ((pa.mean() + pb.mean()) * 1e-3)
+                                      / 1e9, 1)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample of the same workload")
+        line["cpu_baseline"] = cpu_baseline(w, inp, D.cpu().numpy(), args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,28 @@
+// Internal launchers (host side). Arguments are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/bmm.h"
+
+namespace bmm {
+
+struct MmaArgs {
+  float* D;
+  const uint32_t* A;
+  const uint32_t* B;
+  const float* C;  // null -> c_scalar
+  float c_scalar;
+  int64_t batch, M_rep, N_rep, K_rep;
+  int dtype;
+};
+
+hipError_t launch_pack(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
+                       int64_t K, int64_t ld, int R, hipStream_t s);
+hipError_t launch_box(void* dst, const void* src, const bmm_box_desc& d, hipStream_t s);
+hipError_t launch_mma_direct(const MmaArgs& a, hipStream_t s);
+hipError_t launch_mma_tiled(const MmaArgs& a, hipStream_t s);
+hipError_t launch_mma_skinny(const MmaArgs& a, hipStream_t s);
+
+}  // namespace bmm

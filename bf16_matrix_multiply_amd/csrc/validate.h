@@ -1,0 +1,30 @@
+// Host-side argument checks for every entry point. Pure C++ (no HIP calls),
+// so each rejection path runs without a GPU.
+#pragma once
+
+#include <stdint.h>
+#include <string>
+
+#include "../../include/bmm.h"
+
+namespace bmm {
+
+struct Status {
+  int code = BMM_OK;
+  std::string msg;
+  bool ok() const { return code == BMM_OK; }
+};
+
+Status check_pack(const uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
+                  int64_t K, int64_t ld_src, int32_t atom_rows);
+
+Status check_box(const void* dst, const void* src, const bmm_box_desc* d);
+
+Status check_mma(const float* D, const uint32_t* A, const uint32_t* B, const float* C,
+                 int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep, int32_t dtype,
+                 int32_t kernel);
+
+// Largest image (bytes) one box repeat may stage through LDS.
+constexpr int64_t kBoxImageLimit = 65536;
+
+}  // namespace bmm

@@ -1,0 +1,170 @@
+/*
+ * bmm.h — C ABI of the MI355X (gfx950) tiled f16/bf16 multiply-accumulate
+ * D = A * B^T + C with float32 accumulation, over the packed operand layouts
+ * of the Apache TVM "tirx" mma.sync tile-op page.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
+ *     library keeps no reference to it after the call returns.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return once the kernels are enqueued.
+ *   - Arguments are validated on the host, once per call, before any HIP
+ *     call (the cp.async.bulk.tensor page, "Example: two explicit 8x16
+ *     boxes": descriptor set-up is host work, not repeated per box). On a
+ *     failed check nothing is launched and nothing is written.
+ *   - Invalid fields are rejected, never promoted, folded, transposed or
+ *     reinterpreted (cp.async.bulk.tensor page, "Operands and descriptor
+ *     fields"; mma.sync page introduction: no implicit type change, K-atom
+ *     choice or transpose).
+ *   - Return value: BMM_OK (0) or a negative status; bmm_last_error()
+ *     returns a message for the last failure on the calling thread.
+ *   - The library allocates no device memory and keeps no device state.
+ *   - Destination first (mma.sync page, "Operand coordinates and
+ *     ownership": the call takes D, A, B, C).
+ */
+#ifndef BMM_H
+#define BMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { BMM_F16 = 0, BMM_BF16 = 1 } bmm_dtype;
+
+enum {
+  BMM_OK = 0,
+  BMM_EINVAL = -1,   /* bad extent, dtype, field value or null pointer */
+  BMM_EALIGN = -2,   /* pointer or stride not aligned as required */
+  BMM_EOVERLAP = -3, /* destination overlaps a source (other than D == C) */
+  BMM_ERANGE = -4,   /* a box image larger than the staging limit */
+  BMM_EHIP = -5      /* the HIP runtime reported an error at launch */
+};
+
+/* Kernel selection for bmm_mma_tile_with. AUTO picks by shape; the others
+ * force one kernel (every kernel accepts every valid shape). */
+typedef enum {
+  BMM_KERNEL_AUTO = 0,
+  BMM_KERNEL_DIRECT = 1, /* one wave per 16x16 output block, operands straight from HBM */
+  BMM_KERNEL_TILED = 2,  /* LDS-staged 256x256 macro tiles for large M and N */
+  BMM_KERNEL_SKINNY = 3  /* small M: split-K across waves, B streamed once */
+} bmm_kernel;
+
+/*
+ * bmm_pack_operand — row-major halves to packed b32 atoms.
+ *
+ * Defined by the mma.sync page, "Operand coordinates and ownership" (A is
+ * (M_repeat, K_repeat, 16, k/2) and B is (N_repeat, K_repeat, 8, k/2) b32
+ * words, each word two adjacent K values) and the worked example's host
+ * code (row-major halves reshaped, transposed and viewed as uint32, so the
+ * even K value is the low 16 bits). Atom K is k = 16.
+ *
+ *   dst[b, r, kr, i, w] = src[b, R*r+i, 16*kr+2*w] | src[b, R*r+i, 16*kr+2*w+1] << 16
+ *
+ * dst       (batch, rows/R, K/16, R, 8) uint32, contiguous, 16-byte aligned.
+ * src       (batch, rows, ld_src) 16-bit values (f16 or bf16 bits; the bits are
+ *           moved, never converted), batch stride rows*ld_src elements,
+ *           16-byte aligned.
+ * rows      multiple of atom_rows; K multiple of 16; ld_src >= K and a
+ *           multiple of 8 (16-byte row starts). Zero batch, rows or K is a
+ *           no-op.
+ * atom_rows R: 16 for an A operand, 8 for a B operand.
+ * Errors: BMM_EINVAL (extents, atom_rows), BMM_EALIGN, BMM_EOVERLAP (dst and
+ * src overlap), BMM_EHIP.
+ */
+int bmm_pack_operand(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
+                     int64_t K, int64_t ld_src, int32_t atom_rows, void* stream);
+
+/*
+ * bmm_box_copy — a rectangular global box through an LDS image.
+ *
+ * The role of the TMA tile-mode box load on the cp.async.bulk.tensor page
+ * ("Operands and descriptor fields", "Example: two explicit 8x16 boxes"):
+ * for each repeat t the box at coords + t*coord_step is staged into a
+ * shared-memory (LDS) image, laid out with the requested swizzle, and the
+ * image is written out compact and unswizzled:
+ *
+ *   dst_image[t, j_0..j_{rank-1}] = src[coords + t*coord_step + j] if every
+ *                                   coordinate is inside dims, else 0.
+ *
+ * desc fields (outer-to-inner order, as on the page):
+ *   rank        1..5
+ *   elem_bytes  1, 2, 4 or 8 (the storage type; never reinterpreted)
+ *   dims        global extents, each >= 1
+ *   strides     byte strides; strides[rank-1] == elem_bytes; outer strides
+ *               multiples of 16 ("suitably aligned outer byte strides")
+ *   box         1..256 per dimension
+ *   coords      start coordinates; may lie partly or wholly outside dims
+ *   n_repeat    >= 1 repeats (the leading image axis)
+ *   coord_step  per-repeat coordinate increment
+ *   swizzle     0..3: none / 32-byte / 64-byte / 128-byte XOR swizzle of
+ *               the LDS image (internal; the exported image is unswizzled)
+ *   oob_fill    0 (zero fill, the page's default) is the only value accepted
+ * dst_image    (n_repeat, box...) compact, 16-byte aligned; must not overlap src.
+ * src          16-byte aligned base of the global tensor.
+ * bytes_moved  nullable host pointer; receives n_repeat * prod(box) * elem_bytes.
+ * One repeat's image may hold at most 65536 bytes (else BMM_ERANGE).
+ * Errors: BMM_EINVAL, BMM_EALIGN, BMM_EOVERLAP, BMM_ERANGE, BMM_EHIP.
+ */
+typedef struct {
+  int32_t rank;
+  int32_t elem_bytes;
+  int64_t dims[5];
+  int64_t strides[5];
+  int32_t box[5];
+  int64_t coords[5];
+  int32_t n_repeat;
+  int64_t coord_step[5];
+  int32_t swizzle;
+  int32_t oob_fill;
+} bmm_box_desc;
+
+int bmm_box_copy(void* dst_image, const void* src, const bmm_box_desc* desc,
+                 int64_t* bytes_moved, void* stream);
+
+/*
+ * bmm_mma_tile — D = A * B^T + C over packed operands.
+ *
+ * Defined by the mma.sync page: "Operand coordinates and ownership" (the
+ * layouts below; A and B share one input dtype, the accumulator is float32)
+ * and "Accumulation, transpose and alpha/beta" (repeat order batch, M, N,
+ * then K; C is a matching tensor or a scalar broadcast; only the first K
+ * step reads C, later steps read D).
+ *
+ * D  (batch, M_rep, N_rep, 16, 8) float32, written.
+ * A  (batch, M_rep, K_rep, 16, 8) uint32 words (two halves per word, even K low).
+ * B  (batch, N_rep, K_rep, 8, 8)  uint32 words; B's logical axes are (N, K).
+ * C  (batch, M_rep, N_rep, 16, 8) float32, or NULL to use c_scalar for every
+ *    element. C == D (in place) is allowed: each output is read before it is
+ *    written by the same thread. Any other overlap of D with A, B or C is
+ *    rejected.
+ * Every pointer is 16-byte aligned. Extents are >= 0; a zero batch, M_rep or
+ * N_rep is a no-op; K_rep = 0 gives D = C (the empty sum).
+ * Summation order inside the hardware's 32-deep MFMA step is the hardware's;
+ * between steps K is taken in ascending order from C.
+ * Errors: BMM_EINVAL, BMM_EALIGN, BMM_EOVERLAP, BMM_EHIP.
+ */
+int bmm_mma_tile(float* D, const uint32_t* A, const uint32_t* B, const float* C,
+                 float c_scalar, int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep,
+                 bmm_dtype dtype, void* stream);
+
+/* bmm_mma_tile with an explicit kernel choice (bmm_kernel); same contract. */
+int bmm_mma_tile_with(float* D, const uint32_t* A, const uint32_t* B, const float* C,
+                      float c_scalar, int64_t batch, int64_t M_rep, int64_t N_rep,
+                      int64_t K_rep, bmm_dtype dtype, int32_t kernel, void* stream);
+
+/* Which kernel AUTO would run for this shape (a bmm_kernel value), or < 0. */
+int bmm_select_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep);
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* bmm_last_error(void);
+
+/* ABI version: 1. */
+int bmm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BMM_H */

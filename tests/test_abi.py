@@ -1,0 +1,168 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/bmm.h
+declares, and rejects every invalid argument on the host before any HIP call
+(so no GPU is needed; nothing valid is ever launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bf16_matrix_multiply_amd as bmm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bmm.h")
+
+EINVAL, EALIGN, EOVERLAP, ERANGE = -1, -2, -3, -4
+
+# Fake device addresses: only compared and range-checked by the validator,
+# never dereferenced (every call below fails validation first).
+P0, P1, P2, P3 = 0x7F0000000000, 0x7F1000000000, 0x7F2000000000, 0x7F3000000000
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(bmm.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return bmm.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bmm_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    syms = declared_symbols()
+    assert set(syms) >= {"bmm_pack_operand", "bmm_box_copy", "bmm_mma_tile", "bmm_last_error"}
+    for s in syms:
+        assert hasattr(L, s), f"libbmm.so does not export {s}"
+    assert L.bmm_abi_version() == 1
+
+
+def err(L):
+    return L.bmm_last_error().decode()
+
+
+def pack(L, dst=P0, src=P1, batch=1, rows=16, K=32, ld=32, R=16):
+    return L.bmm_pack_operand(dst, src, batch, rows, K, ld, R, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(R=4), EINVAL, "atom_rows"),
+    (dict(rows=24, R=16), EINVAL, "multiple of atom_rows"),
+    (dict(K=40, ld=48), EINVAL, "multiple of 16"),
+    (dict(ld=16), EINVAL, "ld_src"),
+    (dict(batch=-1), EINVAL, "negative"),
+    (dict(K=-16), EINVAL, "negative"),
+    (dict(ld=36), EALIGN, "multiple of 8"),
+    (dict(dst=P0 + 4), EALIGN, "aligned"),
+    (dict(src=P1 + 2), EALIGN, "aligned"),
+    (dict(dst=0), EINVAL, "null"),
+    (dict(dst=P1 + 64), EOVERLAP, "overlaps"),
+])
+def test_pack_rejects(L, kw, code, needle):
+    assert pack(L, **kw) == code
+    assert needle in err(L)
+
+
+def test_pack_empty_is_noop(L):
+    # zero extents never reach HIP and need no pointers
+    assert pack(L, dst=0, src=0, batch=0) == 0
+    assert pack(L, dst=0, src=0, rows=0) == 0
+    assert pack(L, dst=0, src=0, K=0, ld=0) == 0
+
+
+def box_desc(**kw):
+    d = bmm.BoxDesc()
+    d.rank, d.elem_bytes = 2, 4
+    d.dims[0], d.dims[1] = 16, 16
+    d.strides[0], d.strides[1] = 64, 4
+    d.box[0], d.box[1] = 8, 16
+    d.n_repeat = 2
+    d.coord_step[0] = 8
+    for k, v in kw.items():
+        if isinstance(v, tuple):
+            getattr(d, k)[v[0]] = v[1]
+        else:
+            setattr(d, k, v)
+    return d
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(rank=0), EINVAL, "rank"),
+    (dict(rank=6), EINVAL, "rank"),
+    (dict(elem_bytes=3), EINVAL, "elem_bytes"),
+    (dict(box=(0, 0)), EINVAL, "box[0]"),
+    (dict(box=(1, 257)), EINVAL, "box[1]"),
+    (dict(swizzle=4), EINVAL, "swizzle"),
+    (dict(swizzle=-1), EINVAL, "swizzle"),
+    (dict(oob_fill=1), EINVAL, "oob_fill"),
+    (dict(n_repeat=0), EINVAL, "n_repeat"),
+    (dict(dims=(0, 0)), EINVAL, "dims[0]"),
+    (dict(strides=(1, 8)), EINVAL, "innermost stride"),
+    (dict(strides=(0, 72)), EALIGN, "multiple of 16"),
+    (dict(strides=(0, -64)), EINVAL, "positive"),
+    (dict(box=(0, 256), elem_bytes=8, strides=(1, 8)), ERANGE, "limit"),
+])
+def test_box_rejects(L, kw, code, needle):
+    if "box" in kw and kw.get("elem_bytes") == 8:
+        d = box_desc(elem_bytes=8)
+        d.box[0], d.box[1] = 256, 256
+        d.strides[1] = 8
+    else:
+        d = box_desc(**kw)
+    n = ctypes.c_int64(-7)
+    assert L.bmm_box_copy(P0, P1, ctypes.byref(d), ctypes.byref(n), None) == code
+    assert needle in err(L)
+    assert n.value == -7  # untouched on failure
+
+
+def test_box_rejects_pointers(L):
+    d = box_desc()
+    assert L.bmm_box_copy(P0 + 8, P1, ctypes.byref(d), None, None) == EALIGN
+    assert L.bmm_box_copy(0, P1, ctypes.byref(d), None, None) == EINVAL
+    assert L.bmm_box_copy(P1 + 512, P1, ctypes.byref(d), None, None) == EOVERLAP
+    assert L.bmm_box_copy(P0, P1, None, None, None) == EINVAL
+
+
+def mma(L, D=P0, A=P1, B=P2, C=None, batch=1, M=2, N=3, K=4, dtype=1, kernel=0):
+    return L.bmm_mma_tile_with(D, A, B, C, 0.0, batch, M, N, K, dtype, kernel, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(dtype=2), EINVAL, "dtype"),
+    (dict(kernel=7), EINVAL, "kernel"),
+    (dict(M=-1), EINVAL, "negative"),
+    (dict(K=-1), EINVAL, "negative"),
+    (dict(D=0), EINVAL, "D is null"),
+    (dict(A=0), EINVAL, "null"),
+    (dict(D=P0 + 4), EALIGN, "aligned"),
+    (dict(A=P1 + 8), EALIGN, "aligned"),
+    (dict(C=P3 + 4), EALIGN, "aligned"),
+    (dict(D=P1 + 512), EOVERLAP, "overlaps A"),
+    (dict(D=P2), EOVERLAP, "overlaps B"),
+    (dict(C=P0 + 512), EOVERLAP, "partially overlaps C"),
+    (dict(M=1 << 41), EINVAL, "too large"),
+])
+def test_mma_rejects(L, kw, code, needle):
+    assert mma(L, **kw) == code
+    assert needle in err(L)
+
+
+def test_mma_empty_is_noop(L):
+    assert mma(L, D=0, A=0, B=0, batch=0) == 0
+    assert mma(L, D=0, A=0, B=0, M=0) == 0
+    assert mma(L, D=0, A=0, B=0, N=0) == 0
+
+
+def test_plain_entry_point_validates(L):
+    assert L.bmm_mma_tile(P0 + 4, P1, P2, None, 0.0, 1, 1, 1, 1, 1, None) == EALIGN
+
+
+def test_select_kernel(L):
+    assert L.bmm_select_kernel(-1, 1, 1, 1) == EINVAL
+    for shape in [(1, 1, 1, 2), (1, 8, 16, 16), (1, 256, 512, 256), (1, 1, 2048, 1024),
+                  (1, 512, 1024, 512)]:
+        assert L.bmm_select_kernel(*shape) in (1, 2, 3)

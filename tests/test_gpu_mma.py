@@ -1,0 +1,204 @@
+"""GPU parity of bmm_mma_tile against the oracle.
+
+Quarter-integer inputs (every product and partial sum exact in fp32) must be
+bit-exact; normal inputs must satisfy |D - D_ref| <= 1e-3 (|A||B|^T + |C|)
+elementwise. Every kernel accepts every valid shape, so each is forced on the
+same cases, which span several 256-wide tiles and ragged tails in M, N and K.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bf16_matrix_multiply_amd as bmm
+import oracle
+import workloads
+from tests import gpu_util as gu
+from tests import util
+
+pytestmark = pytest.mark.gpu
+
+KERNELS = ["direct", "tiled"]
+
+C = workloads.custom
+SMALL = {
+    # the worked example and the 128x128x256 workload as given
+    "tile_16x8x32_f16": workloads.WORKLOADS["tile_16x8x32_f16"],
+    "gemm_128x128x256_bf16_ctensor": workloads.WORKLOADS["gemm_128x128x256_bf16_ctensor"],
+    # quarter-integer (bit-exact) cases with ragged extents
+    "q_min_1x1x1": C(1, 16, 8, 16, "bf16", "quarter", "quarter", c_scalar=0.25),
+    "q_odd_b2": C(2, 48, 40, 80, "f16", "quarter", "quarter", c_tensor=True),
+    "q_tails_272x264x336": C(1, 272, 264, 336, "bf16", "quarter", "quarter", c_tensor=True),
+    "q_skinny_16x1032x1040": C(1, 16, 1032, 1040, "f16", "quarter", "quarter"),
+    "q_tall_528x24x48": C(1, 528, 24, 48, "bf16", "quarter", "quarter", c_tensor=True),
+    # normal-input cases
+    "n_512x512x512_ct": C(1, 512, 512, 512, "bf16", c_tensor=True),
+    "n_f16_b3_80x136x272": C(3, 80, 136, 272, "f16", c_tensor=True),
+    "n_skinny_64x520x2064": C(1, 64, 520, 2064, "bf16", b_scale=0.02),
+    "n_kodd_32x256x16": C(1, 32, 256, 16, "bf16", c_tensor=True),
+}
+
+
+def inputs(w):
+    return workloads.make_inputs(w, seed=0)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("case", sorted(SMALL))
+def test_small_full_parity(case, kernel):
+    w = SMALL[case]
+    inp = inputs(w)
+    _, _, _, D = gu.gpu_run(w, inp, kernel)
+    gu.assert_parity_full(w, inp, D, kernel)
+
+
+def test_page_example_exact():
+    """The worked 16x8 example: equal to a.f32 @ b.f32.T bit for bit."""
+    w = workloads.WORKLOADS["tile_16x8x32_f16"]
+    inp = inputs(w)
+    _, _, _, D = gu.gpu_run(w, inp)
+    a = inp["a"][0].view(np.float16).astype(np.float32)
+    b = inp["b"][0].view(np.float16).astype(np.float32)
+    assert np.array_equal(util.tile_to_logical(D)[0], a @ b.T)
+
+
+def test_fragment_map_one_hot():
+    """One-hot probes through the real path: with A[m0, k0] = 1 and
+    B[n0, k0] = 1 only, D is 1 at (m0, n0) and 0 elsewhere, for every (m0, n0)
+    of a 16x16 block (batched) and k0 in each lane group of a 32-deep step."""
+    for k0 in (0, 9, 18, 31):
+        batch = 16 * 16
+        a = np.zeros((batch, 16, 32), np.float32)
+        b = np.zeros((batch, 16, 32), np.float32)
+        for bi in range(batch):
+            a[bi, bi // 16, k0] = 1.0
+            b[bi, bi % 16, k0] = 1.0
+        A = bmm.pack_operand(gu.dev_u16(workloads.f32_to_bf16_bits(a)), 16)
+        B = bmm.pack_operand(gu.dev_u16(workloads.f32_to_bf16_bits(b)), 8)
+        for kernel in KERNELS:
+            D = util.tile_to_logical(bmm.mma_tile(A, B, None, 0.0, "bf16", kernel=kernel).cpu().numpy())
+            ref = np.zeros((batch, 16, 16), np.float32)
+            for bi in range(batch):
+                ref[bi, bi // 16, bi % 16] = 1.0
+            assert np.array_equal(D, ref), (k0, kernel)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_scalar_equals_filled_tensor(kernel):
+    w = C(1, 96, 200, 208, "bf16")
+    inp = inputs(w)
+    A, B, _, D1 = gu.gpu_run(w, dict(inp, c_scalar=np.float32(0.375)), kernel)
+    Cf = torch.full((1, w.M_rep, w.N_rep, 16, 8), 0.375, device="cuda")
+    D2 = bmm.mma_tile(A, B, Cf, 0.0, "bf16", kernel=kernel).cpu().numpy()
+    assert np.array_equal(D1, D2)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_in_place_and_k_chaining(kernel):
+    """D == C in place, and the recurrence split over two calls (C -> D -> D):
+    bit-exact against one call on quarter-integer inputs."""
+    w = C(2, 272, 136, 336, "f16", "quarter", "quarter", c_tensor=True)
+    inp = inputs(w)
+    A, B, Cd, D = gu.gpu_run(w, inp, kernel)
+    gu.assert_parity_full(w, inp, D, kernel)
+    Dip = Cd.clone()
+    bmm.mma_tile(A, B, Dip, 0.0, w.dtype, out=Dip, kernel=kernel)
+    assert np.array_equal(Dip.cpu().numpy(), D)
+    cut = 7
+    Dc = Cd.clone()
+    bmm.mma_tile(A[:, :, :cut].contiguous(), B[:, :, :cut].contiguous(), Dc, 0.0, w.dtype,
+                 out=Dc, kernel=kernel)
+    bmm.mma_tile(A[:, :, cut:].contiguous(), B[:, :, cut:].contiguous(), Dc, 0.0, w.dtype,
+                 out=Dc, kernel=kernel)
+    assert np.array_equal(Dc.cpu().numpy(), D)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_k_rep_zero_and_zero_a(kernel):
+    """K_rep = 0 gives D = C; A = 0 gives D = C bitwise."""
+    w = C(1, 64, 64, 64, "bf16", c_tensor=True)
+    inp = inputs(w)
+    Cd = torch.from_numpy(inp["c_tensor"]).cuda()
+    A0 = torch.zeros((1, 4, 0, 16, 8), dtype=torch.int32, device="cuda")
+    B0 = torch.zeros((1, 8, 0, 8, 8), dtype=torch.int32, device="cuda")
+    D = bmm.mma_tile(A0, B0, Cd, 0.0, "bf16", kernel=kernel)
+    assert np.array_equal(D.cpu().numpy(), inp["c_tensor"])
+    Az = torch.zeros((1, 4, 4, 16, 8), dtype=torch.int32, device="cuda")
+    B = bmm.pack_operand(gu.dev_u16(inp["b"]), 8)
+    D = bmm.mma_tile(Az, B, Cd, 0.0, "bf16", kernel=kernel)
+    assert np.array_equal(D.cpu().numpy(), inp["c_tensor"])
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_deterministic_and_stream(kernel):
+    """Two runs give identical bits, also on a non-default stream."""
+    w = C(1, 256, 264, 1040, "bf16", c_tensor=True)
+    inp = inputs(w)
+    A, B, Cd, D1 = gu.gpu_run(w, inp, kernel)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        D2 = bmm.mma_tile(A, B, Cd, 0.0, "bf16", kernel=kernel)
+    s.synchronize()
+    assert np.array_equal(D1, D2.cpu().numpy())
+
+
+def test_errors_write_nothing():
+    """Host-side rejections launch nothing: the output keeps its contents."""
+    w = C(1, 32, 32, 32, "bf16")
+    inp = inputs(w)
+    A = bmm.pack_operand(gu.dev_u16(inp["a"]), 16)
+    B = bmm.pack_operand(gu.dev_u16(inp["b"]), 8)
+    out = torch.full((1, 2, 4, 16, 8), -5.0, device="cuda")
+    L = bmm.lib()
+    d, a, b = out.data_ptr(), A.data_ptr(), B.data_ptr()
+    assert L.bmm_mma_tile(d, a, b, d + 16, 0.0, 1, 2, 4, 2, 1, None) == -3
+    assert "partially overlaps C" in L.bmm_last_error().decode()
+    assert L.bmm_mma_tile(d, a, b, None, 0.0, 1, 2, 4, 2, 7, None) == -1
+    assert L.bmm_mma_tile(d + 4, a, b, None, 0.0, 1, 2, 4, 2, 1, None) == -2
+    with pytest.raises(ValueError):
+        bmm.mma_tile(A, B[:, :, :1], None, 0.0, "bf16", out=out)
+    torch.cuda.synchronize()
+    assert (out == -5.0).all()
+
+
+# ---- full-size workloads, checked on sampled outputs and exact properties ----
+
+def test_full_gemm_4096_f16_quarter():
+    """4096^3 f16 quarter integers: sampled outputs bit-exact, and every row
+    and column sum of 16*D equal to its int64 closed form."""
+    w = workloads.WORKLOADS["gemm_4096_f16_quarter"]
+    inp = inputs(w)
+    _, _, _, D = gu.gpu_run(w, inp)
+    gu.assert_parity_sampled(w, inp, D)
+    Dl = util.tile_to_logical(D)[0].astype(np.float64)
+    D16 = np.rint(Dl * 16).astype(np.int64)
+    assert np.array_equal(D16.astype(np.float64), Dl * 16)
+    ai = np.rint(4 * util.decode(inp["a"][0], "f16")).astype(np.int64)
+    bi = np.rint(4 * util.decode(inp["b"][0], "f16")).astype(np.int64)
+    assert np.array_equal(D16.sum(axis=1), ai @ bi.sum(axis=0))
+    assert np.array_equal(D16.sum(axis=0), bi @ ai.sum(axis=0))
+
+
+def test_full_skinny_bf16():
+    w = workloads.WORKLOADS["skinny_16x16384x16384_bf16"]
+    inp = inputs(w)
+    _, _, _, D = gu.gpu_run(w, inp)
+    gu.assert_parity_sampled(w, inp, D, count=4096)
+
+
+def test_full_gemm_8192_bf16_ctensor():
+    w = workloads.WORKLOADS["gemm_8192_bf16_ctensor"]
+    inp = inputs(w)
+    _, _, _, D = gu.gpu_run(w, inp)
+    gu.assert_parity_sampled(w, inp, D)
+
+
+@pytest.mark.parametrize("name", ["skinny_16x16384x16384_bf16", "gemm_8192_bf16_ctensor"])
+def test_full_quantised_variants(name):
+    """The large bf16 shapes with quarter-integer operands: bit-exact samples
+    (|D| <= K with a 1/16 grid needs at most 19 bits)."""
+    base = workloads.WORKLOADS[name]
+    w = C(base.batch, base.M, base.N, base.K, "bf16", "quarter", "quarter",
+          c_tensor=False, name=name + "_quarter")
+    inp = workloads.make_inputs(w, seed=1)
+    _, _, _, D = gu.gpu_run(w, inp)
+    gu.assert_parity_sampled(w, inp, D)

@@ -1,0 +1,105 @@
+"""GPU parity of bmm_pack_operand and bmm_box_copy against the oracle:
+bit-exact (these move bits, never values)."""
+import numpy as np
+import pytest
+import torch
+
+import bf16_matrix_multiply_amd as bmm
+import oracle
+import workloads
+from tests import gpu_util as gu
+from tests import util
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("R", [16, 8])
+def test_pack_all_bit_patterns(R):
+    """Every 16-bit pattern (NaN and Inf encodings included) lands bit-exactly
+    where the oracle packer puts it, for several batches."""
+    x = np.arange(1 << 17, dtype=np.uint32).astype(np.uint16).reshape(2, 256, 256)
+    got = gu.host_u32(bmm.pack_operand(gu.dev_u16(x), R))
+    assert np.array_equal(got, oracle.pack(x, R))
+
+
+@pytest.mark.parametrize("R,rows,K,ld", [(16, 16, 16, 16), (8, 8, 32, 40), (16, 48, 80, 96),
+                                         (8, 40, 2064, 2072), (16, 272, 336, 336)])
+def test_pack_shapes_and_row_padding(R, rows, K, ld):
+    rng = np.random.default_rng(rows + K)
+    x = util.random_bits(rng, (3, rows, ld))
+    got = gu.host_u32(bmm.pack_operand(gu.dev_u16(x), R, K=K))
+    assert np.array_equal(got, oracle.pack(x, R, K=K))
+
+
+def test_pack_full_size_operands():
+    """The 8192x8192 and 16384x16384 operands of the large workloads."""
+    rng = np.random.default_rng(0)
+    for rows, K, R in ((8192, 8192, 16), (16384, 16384, 8)):
+        x = workloads.draw_operand(rng, "normal", (1, rows, K), "bf16")
+        got = gu.host_u32(bmm.pack_operand(gu.dev_u16(x), R))
+        assert np.array_equal(got, oracle.pack(x, R)), (rows, K, R)
+        del got, x
+
+
+def test_pack_empty_and_errors():
+    x = torch.zeros((1, 16, 32), dtype=torch.int16, device="cuda")
+    assert bmm.pack_operand(x[:, :0], 16).numel() == 0
+    # a host-side rejection writes nothing
+    bad = torch.zeros((1, 24, 32), dtype=torch.int16, device="cuda")
+    sentinel = torch.full((1, 1, 2, 16, 8), 7, dtype=torch.int32, device="cuda")
+    with pytest.raises(bmm.BmmError, match="multiple of atom_rows"):
+        bmm.pack_operand(bad, 16, out=sentinel)
+    torch.cuda.synchronize()
+    assert (sentinel == 7).all()
+
+
+def test_box_page_example():
+    """Two 8x16 uint32 boxes at (0,0) and (8,0): the image read back is the
+    16x16 input, 1024 bytes for the two boxes."""
+    g = util.golden("tma_two_box_example.json")
+    x = np.arange(256, dtype=np.uint32).reshape(16, 16)
+    xd = torch.from_numpy(x.view(np.int32)).cuda()
+    for swz in range(4):
+        img, nbytes = bmm.box_copy(xd, g["box"], g["coords"], g["n_repeat"], g["coord_steps"][0],
+                                   swizzle=swz)
+        torch.cuda.synchronize()
+        assert tuple(img.shape) == tuple(g["image_shape"])
+        assert nbytes == g["bytes_per_barrier_phase"]
+        assert np.array_equal(img.cpu().numpy().view(np.uint32).reshape(16, 16), x)
+
+
+BOX_CASES = [
+    (np.uint32, (16, 16), (8, 16), (-3, 5), 3, (6, -4)),
+    (np.uint16, (5, 7, 64), (4, 4, 40), (3, -2, 4), 2, (-4, 3, 1)),
+    (np.uint8, (3, 112), (2, 128), (0, -20), 2, (1, 25)),
+    (np.int64, (9, 12), (3, 5), (0, 0), 4, (3, 3)),
+    (np.uint16, (2, 3, 4, 5, 16), (2, 2, 3, 4, 16), (0, 1, -1, 2, 0), 3, (1, 0, 1, -1, 8)),
+    (np.uint32, (300, 64), (256, 64), (20, 0), 1, (0, 0)),
+]
+
+
+@pytest.mark.parametrize("swizzle", [0, 1, 2, 3])
+@pytest.mark.parametrize("case", range(len(BOX_CASES)))
+def test_box_matches_oracle(case, swizzle):
+    dtype, shape, box, coords, rep, step = BOX_CASES[case]
+    rng = np.random.default_rng(case)
+    x = rng.integers(1, 120, shape).astype(dtype)
+    ref, ref_bytes = oracle.box_copy(x, box, coords, rep, step)
+    tdt = {1: torch.uint8, 2: torch.int16, 4: torch.int32, 8: torch.int64}[x.itemsize]
+    xd = torch.from_numpy(x.view({1: np.uint8, 2: np.int16, 4: np.int32, 8: np.int64}[x.itemsize])).cuda()
+    assert xd.dtype == tdt
+    img, nbytes = bmm.box_copy(xd, box, coords, rep, step, swizzle=swizzle)
+    torch.cuda.synchronize()
+    assert nbytes == ref_bytes
+    assert np.array_equal(img.cpu().numpy().view(x.dtype), ref)
+
+
+def test_box_errors_leave_output():
+    x = torch.arange(256, dtype=torch.int32, device="cuda").reshape(16, 16)
+    out = torch.full((1, 8, 16), -1, dtype=torch.int32, device="cuda")
+    with pytest.raises(bmm.BmmError, match="swizzle"):
+        bmm.box_copy(x, (8, 16), (0, 0), 1, swizzle=5, out=out)
+    with pytest.raises(bmm.BmmError, match="box"):
+        bmm.box_copy(x, (8, 300), (0, 0), 1, out=out)
+    torch.cuda.synchronize()
+    assert (out == -1).all()

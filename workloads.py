@@ -13,8 +13,9 @@ B, C):
   result with two K16 issues"). These values are exact in f16 and bf16.
 * ``normal``: ``standard_normal(float32) * scale``, rounded once to bf16 with
   round-to-nearest-even (or to f16 with numpy's own round-to-nearest-even).
-* C, when it is a tensor, is standard normal float32 drawn directly in the
-  atom-tiled accumulator layout (batch, M/16, N/8, 16, 8); the draws are
+* C, when it is a tensor, is standard normal float32 (or, for the exact
+  quarter-integer cases, integers in [-64, 64] divided by 4) drawn directly in
+  the atom-tiled accumulator layout (batch, M/16, N/8, 16, 8); the draws are
   i.i.d., so drawing in the stored layout changes no statistics.
 
 Half-precision operands are returned as uint16 bit patterns, row-major
@@ -61,6 +62,7 @@ class Workload:
     c_tensor: bool = False
     c_scalar: float = 0.0
     exact: bool = False   # every product and partial sum is exact in fp32
+    c_dist: str = "normal"  # "quarter" keeps C on the exact grid as well
 
     @property
     def M_rep(self) -> int:
@@ -135,11 +137,16 @@ def make_inputs(w: Workload, seed: int = 0, a_dist: str | None = None,
     b = draw_operand(rng, b_dist or w.b_dist, (w.batch, w.N, w.K), w.dtype, w.b_scale)
     c = None
     if w.c_tensor:
-        c = rng.standard_normal((w.batch, w.M_rep, w.N_rep, 16, 8), dtype=np.float32)
+        shape = (w.batch, w.M_rep, w.N_rep, 16, 8)
+        if w.c_dist == "quarter":
+            c = (rng.integers(-64, 65, shape) / 4).astype(np.float32)
+        else:
+            c = rng.standard_normal(shape, dtype=np.float32)
     return dict(a=a, b=b, c_tensor=c, c_scalar=np.float32(w.c_scalar))
 
 
 def custom(batch, M, N, K, dtype=BF16, a_dist="normal", b_dist="normal", c_tensor=False,
            c_scalar=0.0, b_scale=1.0, name="custom") -> Workload:
+    exact = a_dist == "quarter" and b_dist == "quarter"
     return Workload(name, batch, M, N, K, dtype, a_dist, b_dist, b_scale, c_tensor, c_scalar,
-                    exact=(a_dist == "quarter" and b_dist == "quarter"))
+                    exact=exact, c_dist="quarter" if exact else "normal")
