@@ -16,7 +16,6 @@ workload on this host's cores.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -28,28 +27,16 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 import workloads  # noqa: E402
+from bf16_matrix_multiply_amd.profile_run import source_sha  # noqa: E402
 
 METRIC = "TFLOP/s for f16/bf16 A·Bᵀ+C (fp32 acc) and % of MFMA/HBM roofline"
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}   # MI355X dense, published
 PEAK_HBM_GBS = 8000.0                                  # MI355X HBM3E, published
 RIDGE_FLOP_PER_BYTE = 2500e12 / 8000e9
-KERNEL_SOURCES = {
-    "mma_tile": ["mma_direct.hip", "mma_tiled.hip", "mma_skinny.hip", "common.h"],
-    "pack_operand": ["pack.hip", "common.h"],
-}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
-
-
-def source_sha(kernel: str) -> str:
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kernel]:
-        p = os.path.join(ROOT, "bf16_matrix_multiply_amd", "csrc", f)
-        if os.path.exists(p):
-            h.update(open(p, "rb").read())
-    return h.hexdigest()[:16]
 
 
 def traffic_from_profiles(kernel: str, workload: str):

@@ -30,7 +30,7 @@ int hip_status(hipError_t e, const char* what) {
 // wave per 16 x 16 block.
 int choose_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep) {
   const int64_t macro_tiles = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
-  if (macro_tiles >= 128) return BMM_KERNEL_TILED;
+  if (macro_tiles >= 128 && K_rep < bmm::kTiledMaxKRep) return BMM_KERNEL_TILED;
   if (M_rep <= 4 && N_rep * K_rep >= 65536) return BMM_KERNEL_SKINNY;
   return BMM_KERNEL_DIRECT;
 }
@@ -81,7 +81,12 @@ int bmm_mma_tile_with(float* D, const uint32_t* A, const uint32_t* B, const floa
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (kernel) {
     case BMM_KERNEL_DIRECT: return hip_status(bmm::launch_mma_direct(a, s), "mma_tile direct launch");
-    case BMM_KERNEL_TILED: return hip_status(bmm::launch_mma_tiled(a, s), "mma_tile tiled launch");
+    case BMM_KERNEL_TILED:
+      if (K_rep >= bmm::kTiledMaxKRep) {
+        g_last_error = "mma_tile: the tiled kernel takes K_rep < 262144";
+        return BMM_EINVAL;
+      }
+      return hip_status(bmm::launch_mma_tiled(a, s), "mma_tile tiled launch");
     default: return hip_status(bmm::launch_mma_skinny(a, s), "mma_tile skinny launch");
   }
 }

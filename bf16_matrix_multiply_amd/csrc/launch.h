@@ -22,6 +22,9 @@ hipError_t launch_pack(uint32_t* dst, const uint16_t* src, int64_t batch, int64_
                        int64_t K, int64_t ld, int R, hipStream_t s);
 hipError_t launch_box(void* dst, const void* src, const bmm_box_desc& d, hipStream_t s);
 hipError_t launch_mma_direct(const MmaArgs& a, hipStream_t s);
+// The tiled kernel addresses one tile's operands with 32-bit buffer offsets:
+// it takes K_rep < 2^18 (K < 4M).
+constexpr int64_t kTiledMaxKRep = int64_t(1) << 18;
 hipError_t launch_mma_tiled(const MmaArgs& a, hipStream_t s);
 hipError_t launch_mma_skinny(const MmaArgs& a, hipStream_t s);
 

@@ -25,6 +25,8 @@
 // linear tile index is remapped so each XCD receives a contiguous run of
 // tiles, and runs are rasterised in bands of 8 M tiles, so the tiles that
 // share A rows and B columns run on the same XCD and share its L2.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -42,6 +44,12 @@ constexpr int kLoadsB = kChunksB / kThreads;              // 8 per thread
 constexpr int kStageBytes = (kChunksA + kChunksB) * 16;   // 64 KB
 constexpr int kBOffset = kChunksA * 16;
 constexpr int kXcds = 8;
+// Buffer-resource word 3 for raw (unswizzled, untyped) loads on CDNA, and an
+// offset that every resource here treats as out of range (reads return 0).
+constexpr int kBufferFlags = 0x00020000;
+constexpr uint32_t kOutOfRange = 0x7fffffffu;
+// s_waitcnt immediate: vmcnt(0), expcnt and lgkmcnt at their maxima (no wait).
+constexpr int kWaitVmcnt0 = 0x0f70;
 constexpr int kGroupM = 8;
 
 // Half-swap of a 32-byte LDS row (see the file comment). A atoms have 16
@@ -84,30 +92,34 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
   const int64_t m_atom0 = tc.mt * kTileMAtoms, n_atom0 = tc.nt * kTileNAtoms;
   const int64_t K_rep = p.K_rep;
 
-  // ---- per-thread staging addresses ----
+  // ---- per-thread staging offsets ----
   // Chunk q = r * 256 + tid of a slab. For A (128 chunks per M atom) the M
   // atom is 2r + tid/128 and the K atom, row and half depend on tid only; for
-  // B (64 chunks per N atom) the N atom is 4r + tid/64. So each operand needs
-  // one base pointer, an atom-row stride per r, and LDS offsets r * 4096 + c.
+  // B (64 chunks per N atom) the N atom is 4r + tid/64. Loads go through
+  // buffer resources based at the tile's first atom row, whose size ends at
+  // the operand's last row: rows past M_rep (N_rep) fall outside and read as
+  // zero, and K atoms past K_rep are pushed outside explicitly.
   const int a_t = tid >> 7, a_j = (tid >> 5) & 3, a_m = (tid >> 1) & 15, a_h = tid & 1;
-  const int64_t a_row0 = m_atom0 + a_t;
-  const uint32_t* a_base = p.A + ((tc.b * p.M_rep + a_row0) * K_rep + a_j) * kAtomWordsA +
-                           a_m * 8 + a_h * 4;
-  const int64_t a_rstride = 2 * K_rep * kAtomWordsA;  // words between r and r + 1
-  const int a_lds = (a_t * kSlabKAtoms + a_j) * 512 + a_m * 32 + 16 * (a_h ^ swz_a(a_m));
   const int b_t = tid >> 6, b_j = (tid >> 4) & 3, b_r = (tid >> 1) & 7, b_h = tid & 1;
-  const int64_t b_row0 = n_atom0 + b_t;
-  const uint32_t* b_base = p.B + ((tc.b * p.N_rep + b_row0) * K_rep + b_j) * kAtomWordsB +
-                           b_r * 8 + b_h * 4;
-  const int64_t b_rstride = 4 * K_rep * kAtomWordsB;
+  const int64_t a_row_bytes = K_rep * 512, b_row_bytes = K_rep * 256;
+  const int64_t a_left = (p.M_rep - m_atom0) * a_row_bytes;
+  const int64_t b_left = (p.N_rep - n_atom0) * b_row_bytes;
+  const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(p.A + (tc.b * p.M_rep + m_atom0) * K_rep * kAtomWordsA), 0,
+      int(a_left < kOutOfRange ? a_left : kOutOfRange), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint32_t*>(p.B + (tc.b * p.N_rep + n_atom0) * K_rep * kAtomWordsB), 0,
+      int(b_left < kOutOfRange ? b_left : kOutOfRange), kBufferFlags);
+  uint32_t a_voff[kLoadsA], b_voff[kLoadsB];
+#pragma unroll
+  for (int r = 0; r < kLoadsA; ++r)
+    a_voff[r] = uint32_t((2 * r + a_t) * a_row_bytes + a_j * 512 + a_m * 32 + a_h * 16);
+#pragma unroll
+  for (int r = 0; r < kLoadsB; ++r)
+    b_voff[r] = uint32_t((4 * r + b_t) * b_row_bytes + b_j * 256 + b_r * 32 + b_h * 16);
+  const int a_lds = (a_t * kSlabKAtoms + a_j) * 512 + a_m * 32 + 16 * (a_h ^ swz_a(a_m));
   const int b_lds =
       kBOffset + (b_t * kSlabKAtoms + b_j) * 256 + b_r * 32 + 16 * (b_h ^ swz_b(b_t, b_r));
-  // rows of this tile that exist (ragged last tiles): bit r set if chunk group r is in range
-  uint32_t a_rows_ok = 0, b_rows_ok = 0;
-#pragma unroll
-  for (int r = 0; r < kLoadsA; ++r) a_rows_ok |= uint32_t(a_row0 + 2 * r < p.M_rep) << r;
-#pragma unroll
-  for (int r = 0; r < kLoadsB; ++r) b_rows_ok |= uint32_t(b_row0 + 4 * r < p.N_rep) << r;
 
   // ---- per-lane fragment offsets in a stage ----
   const int m = lane & 15, g = lane >> 4;
@@ -117,29 +129,28 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
                      16 * ((g & 1) ^ swz_b(nb_atom, rr));
 
   const int64_t n_slabs = (K_rep + kSlabKAtoms - 1) / kSlabKAtoms;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  u32x4 ra[kLoadsA], rb[kLoadsB];
+  u32x4 ga[kLoadsA], gb[kLoadsB];   // one slab in flight from HBM / L2
 
   auto load_slab = [&](int64_t s) {
-    const int64_t k0 = s * kSlabKAtoms;
-    const bool a_k = k0 + a_j < K_rep, b_k = k0 + b_j < K_rep;
-    const uint32_t* pa = a_base + k0 * kAtomWordsA;
-    const uint32_t* pb = b_base + k0 * kAtomWordsB;
+    const int32_t koff_a = int32_t(s * kSlabKAtoms * 512), koff_b = int32_t(s * kSlabKAtoms * 256);
+    const bool a_k = s * kSlabKAtoms + a_j < K_rep, b_k = s * kSlabKAtoms + b_j < K_rep;
 #pragma unroll
     for (int r = 0; r < kLoadsA; ++r)
-      ra[r] = (a_k && ((a_rows_ok >> r) & 1)) ? load16(pa + r * a_rstride) : zero;
+      ga[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            a_rsrc, a_k ? a_voff[r] : kOutOfRange, koff_a, 0));
 #pragma unroll
     for (int r = 0; r < kLoadsB; ++r)
-      rb[r] = (b_k && ((b_rows_ok >> r) & 1)) ? load16(pb + r * b_rstride) : zero;
+      gb[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            b_rsrc, b_k ? b_voff[r] : kOutOfRange, koff_b, 0));
   };
   auto store_slab = [&](int stage) {
     char* base = smem + stage * kStageBytes;
 #pragma unroll
     for (int r = 0; r < kLoadsA; ++r)
-      *reinterpret_cast<u32x4*>(base + a_lds + r * (kThreads * 16)) = ra[r];
+      *reinterpret_cast<u32x4*>(base + a_lds + r * (kThreads * 16)) = ga[r];
 #pragma unroll
     for (int r = 0; r < kLoadsB; ++r)
-      *reinterpret_cast<u32x4*>(base + b_lds + r * (kThreads * 16)) = rb[r];
+      *reinterpret_cast<u32x4*>(base + b_lds + r * (kThreads * 16)) = gb[r];
   };
 
   // The first slab goes to LDS before C is loaded, so the staging registers
@@ -196,19 +207,53 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
       for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_16x16x32<DT>(bf[nb], af[mb], acc[mb][nb]);
   };
 
-  for (int64_t s = 0; s < n_slabs; ++s) {
+  // Software pipeline, one barrier per slab. Entering iteration s: slab s is
+  // in LDS stage s&1, the first step's fragments F0 of slab s are in
+  // registers, and slab s+1 is in flight into ga/gb.
+  //   1. read F1 (second step of slab s) from LDS      | 64 MFMAs on F0
+  //   2. write slab s+1 from ga/gb into the other stage |
+  //   3. issue the global loads of slab s+2             |
+  //   4. barrier (slab s+1 visible; stage s&1 no longer read)
+  //   5. read F0 of slab s+1                            | 64 MFMAs on F1
+  u32x4 bf0[8], af0[8], bf1[8], af1[8];
+  if (n_slabs > 0) read_frags(smem, 0, bf0, af0);
+  // Let C land before the loop, so no wait inside the loop is charged to it
+  // (vmcnt(0), other counters untouched).
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  if (n_slabs > 1) load_slab(1);
+  // One slab. kWrite: slab s+1 exists (write it to LDS, read its first
+  // fragments after the barrier); kLoad: slab s+2 exists (issue its loads).
+  // The body has no branches, and scheduling groups interleave the LDS writes
+  // and the global loads with the MFMAs instead of leaving them behind them.
+  auto slab = [&](int64_t s, auto write_tag, auto load_tag) {
+    constexpr bool kWrite = decltype(write_tag)::value, kLoad = decltype(load_tag)::value;
     const int stage = int(s & 1);
-    const bool more = s + 1 < n_slabs;
     const char* base = smem + stage * kStageBytes;
-    u32x4 bf0[8], af0[8], bf1[8], af1[8];
-    read_frags(base, 0, bf0, af0);
-    if (more) load_slab(s + 1);
-    read_frags(base, 1, bf1, af1);   // in flight during the first step's MFMAs
+    read_frags(base, 1, bf1, af1);
     mfma_step(bf0, af0);
-    mfma_step(bf1, af1);
-    if (more) store_slab(stage ^ 1);
+    if constexpr (kWrite) store_slab(stage ^ 1);
+    if constexpr (kLoad) load_slab(s + 2);
+    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);   // 16 LDS fragment reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // 16 MFMAs
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // 2 MFMAs
+      if constexpr (kWrite) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+      if constexpr (kLoad) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);   // last 16 MFMAs
     __syncthreads();
-  }
+    if constexpr (kWrite) read_frags(smem + (stage ^ 1) * kStageBytes, 0, bf0, af0);
+    mfma_step(bf1, af1);
+    if constexpr (kWrite) __builtin_amdgcn_sched_group_barrier(0x100, 16, 1);
+    __builtin_amdgcn_sched_group_barrier(0x008, 64, 1);
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  int64_t s = 0;
+  for (; s + 2 < n_slabs; ++s) slab(s, T{}, T{});
+  if (s + 1 < n_slabs) slab(s++, T{}, F{});
+  if (s < n_slabs) slab(s, F{}, F{});
 
   // ---- epilogue: 16-byte stores, one 1 KB contiguous block per MFMA block ----
   if (interior) {
@@ -234,6 +279,8 @@ hipError_t launch_mma_tiled(const MmaArgs& a, hipStream_t s) {
   const int64_t NT = (a.N_rep + kTileNAtoms - 1) / kTileNAtoms;
   const int64_t n_tiles = a.batch * MT * NT;
   if (n_tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
+  // Buffer offsets inside one tile's 16 A atom rows must stay below 2^31.
+  if (a.K_rep >= kTiledMaxKRep) return hipErrorInvalidValue;
   auto kern = a.dtype == kBF16 ? (a.C ? mma_tiled_kernel<kBF16, true> : mma_tiled_kernel<kBF16, false>)
                                : (a.C ? mma_tiled_kernel<kF16, true> : mma_tiled_kernel<kF16, false>);
   hipLaunchKernelGGL(kern, dim3(unsigned(n_tiles)), dim3(kThreads), 0, s, a, n_tiles, MT, NT);

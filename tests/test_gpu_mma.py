@@ -17,7 +17,7 @@ from tests import util
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = ["direct", "tiled"]
+KERNELS = ["direct", "tiled", "skinny"]
 
 C = workloads.custom
 SMALL = {
