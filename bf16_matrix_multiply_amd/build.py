@@ -45,6 +45,10 @@ def sources():
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
+    current = {f + ".o" for f in sources()}
+    for stale in set(os.listdir(BUILD)) - current:
+        if stale.endswith(".o"):
+            os.remove(os.path.join(BUILD, stale))
     jobs = []
     for f in sources():
         src = os.path.join(CSRC, f)

@@ -106,10 +106,11 @@ def summarize(fetch_csv, write_csv, workload, kernel):
     total = 0.0
     for path, counter, key in ((fetch_csv, "FETCH_SIZE", "fetch"), (write_csv, "WRITE_SIZE", "write")):
         d = _per_dispatch(_rows(path), counter)
-        ids = sorted(d)
-        copy_kib = d[ids[0]][1]                      # first dispatch: the calibration copy
+        # the calibration dispatch is the device-to-device copy (its name says copy)
+        copy_ids = [i for i, (n, _) in d.items() if "copy" in n.lower()]
+        copy_kib = d[copy_ids[0]][1]
         scale = (COPY_BYTES / 1024) / copy_kib if copy_kib > 0 else float("nan")
-        mine = [v for i, (n, v) in d.items() if i != ids[0] and KERNEL_MATCH[kernel] in n]
+        mine = [v for i, (n, v) in d.items() if KERNEL_MATCH[kernel] in n]
         kib = sum(mine) / len(mine)
         rec[f"{key}_kib_per_dispatch_raw"] = round(kib, 1)
         rec[f"{key}_copy_kib_raw"] = round(copy_kib, 1)
