@@ -4,31 +4,43 @@
 // mma_direct.hip (mma.sync page of the TVM tirx docs: "Operand coordinates and
 // ownership"; "Accumulation, transpose and alpha/beta").
 //
-// Macro tile 256 (M) x 256 (N), 4 waves in a 2 x 2 grid, each wave owning a
-// 128 x 128 block of D = 8 x 8 MFMA blocks of 16 x 16 (64 accumulators of 4
-// floats per lane, held in AGPRs). K advances in slabs of 32 (2 K atoms, one
-// MFMA step).
+// Instruction: v_mfma_f32_32x32x16_{bf16,f16}. Measured on MI355X with one
+// wave per SIMD, a stream of independent 32x32x16 operations issues at its
+// full 32 cycles each (2.2 PFLOP/s chip-wide), while 16x16x32 operations
+// issue only every ~27 cycles for 16 cycles of work (1.4 PFLOP/s); at two
+// waves per SIMD (this kernel) the 32-wide form still leads, 2.29 against
+// 2.04 PFLOP/s.
+//
+// Fragment map (B fed as the first operand, A as the second, so the result is
+// D transposed): lane l supplies row n = l % 32 of a 32-column block of B and
+// row m = l % 32 of a 32-row block of A, each with the 8 K values of half
+// l / 32 of one K atom (16 K values per operation). It receives 16 floats:
+// register r = 4q + t holds D[m = l % 32][n = 8q + 4 * (l / 32) + t], i.e.
+// for each q one contiguous 16-byte piece of N atom q of the block.
+//
+// Macro tile 256 (M) x 256 (N), 8 waves (two per SIMD) in a 2 x 4 grid, each
+// wave owning a 128 x 64 block of D = 4 x 2 blocks of 32 x 32 (8 accumulators
+// of 16 floats per lane, held in AGPRs). The two waves of a SIMD run the same
+// pipeline, so while one waits on a load or a barrier the other issues MFMAs.
+// K advances in slabs of 32 (2 K atoms).
 //
 // Staging takes the role the pages give to TMA box loads ("cp.async.bulk.
-// tensor" page): per slab, the A box is 16 M atoms x 2 K atoms (16 pieces of
-// 1 KB, each contiguous in HBM) and the B box 32 N atoms x 2 K atoms (32
-// pieces of 512 B). They are moved by direct-to-LDS buffer loads (each lane's
-// 16 bytes land at M0 + 16 * lane), four slabs deep: a ring of four 32 KB LDS
-// stages, with slab s+4 loaded into the stage slab s has just left. Rows past
-// M_rep / N_rep and K atoms past K_rep read as zero through the buffer range
-// check, so the loop has no branches; slabs past the end are loaded as zeros
-// and multiplied harmlessly, so the ring always holds three slabs in flight.
+// tensor" page). The LDS image of a slab is fragment-major: 16 A fragments
+// (8 row blocks x 2 K atoms) and 16 B fragments of 1 KB each, every fragment
+// stored in lane order, so one direct-to-LDS buffer load (each lane's 16
+// bytes land at M0 + 16 * lane) writes exactly one fragment, gathered from
+// two A atoms or four B atoms in HBM, and one ds_read_b128 per lane reads it
+// back contiguously (no bank conflicts). Loads run four slabs deep: a ring of
+// four 32 KB stages, with slab s+4 loaded into the stage slab s has just left.
+// Rows past M_rep / N_rep and K atoms past K_rep read as zero through the
+// buffer range check, so the loop has no branches; slabs past the end load as
+// zeros and are multiplied harmlessly.
 //
-// Per slab each wave: 32 MFMAs on the fragments already in registers; wait for
-// its own loads of the next slab and for its fragment reads; barrier; issue
-// the loads of slab s+4; read the next slab's fragments; 32 more MFMAs. The
-// barrier is a bare s_barrier with counted waits, so loads of later slabs stay
-// in flight across it.
-//
-// LDS image: atoms are stored whole (32-byte rows); the lane that loads a
-// chunk is chosen so that the two 16-byte halves of a row are swapped on a
-// row-dependent XOR, which spreads a fragment read (lane l takes row l % 16,
-// half (l / 16) % 2) over the banks.
+// Per slab each wave: the MFMAs of the first K atom on fragments already in
+// registers; wait for its own loads of the next slab and its fragment reads;
+// barrier; issue the loads of slab s+4; read the next slab's fragments; the
+// MFMAs of the second K atom. The barrier is a bare s_barrier after a counted
+// wait, so the loads of later slabs stay in flight across it.
 //
 // Work order: workgroups are dispatched round-robin over the 8 XCDs; the
 // linear tile index is remapped so each XCD receives a contiguous run of
@@ -40,14 +52,17 @@
 namespace bmm {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kWaveBlocksM = 4;   // 32-row blocks per wave
+constexpr int kWaveBlocksN = 2;   // 32-column blocks per wave
 constexpr int kTileMAtoms = 16;   // 256 rows
 constexpr int kTileNAtoms = 32;   // 256 columns
-constexpr int kSlabKAtoms = 2;    // 32 K values: one MFMA step
-constexpr int kChunksA = kTileMAtoms * kSlabKAtoms * 32;  // 16-byte chunks per A slab (1024)
-constexpr int kChunksB = kTileNAtoms * kSlabKAtoms * 16;  // (1024)
-constexpr int kLoadsA = kChunksA / kThreads;              // 4 per thread
-constexpr int kLoadsB = kChunksB / kThreads;              // 4 per thread
+constexpr int kSlabKAtoms = 2;    // 32 K values
+constexpr int kFragsA = 16;       // per slab: 8 blocks of 32 rows x 2 K atoms
+constexpr int kFragsB = 16;       // per slab: 8 blocks of 32 columns x 2 K atoms
+constexpr int kLoadsA = kFragsA / kWaves;                 // per wave and slab, one fragment each
+constexpr int kLoadsB = kFragsB / kWaves;
 constexpr int kLoadsPerSlab = kLoadsA + kLoadsB;
 constexpr int kStages = 4;
 constexpr int kXcds = 8;
@@ -64,19 +79,25 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
 }
 constexpr int kWaitVmcnt0 = waitcnt_imm(0, 15);
 
+// One ring stage: fragment f of each operand is 64 lanes x 16 bytes.
 struct Stage {
-  u32x4 a[kChunksA];
-  u32x4 b[kChunksB];
+  u32x4 a[kFragsA][kWave];
+  u32x4 b[kFragsB][kWave];
 };
 
-// LDS-qualified views, so that volatile reads stay ds_read instructions.
-typedef __attribute__((address_space(3))) const char lds_cchar;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-// Half-swap of a 32-byte LDS row (see the file comment). A atoms have 16
-// rows; B atoms have 8 and alternate parity with the N atom index.
-__device__ __forceinline__ int swz_a(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
-__device__ __forceinline__ int swz_b(int atom, int row) { return ((row >> 2) ^ atom) & 1; }
+template <int DT>
+__device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 x, u32x4 y, f32x16 acc) {
+  if constexpr (DT == kBF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x),
+                                                   __builtin_bit_cast(bf16x8, y), acc, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, x),
+                                                  __builtin_bit_cast(f16x8, y), acc, 0, 0, 0);
+  }
+}
 
 struct TileCoord {
   int64_t b, mt, nt;
@@ -110,20 +131,17 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const TileCoord tc = tile_of(blockIdx.x, n_tiles, MT, NT);
   const int64_t m_atom0 = tc.mt * kTileMAtoms, n_atom0 = tc.nt * kTileNAtoms;
   const int64_t K_rep = p.K_rep;
 
   // ---- direct-to-LDS staging ----
-  // LDS chunk q = r * 256 + tid of a stage region is written by lane tid % 64
-  // of wave tid / 64 in load r. A region: M atom q >> 6 = 4r + wave, K atom
-  // (q >> 5) & 1, row (q >> 1) & 15, stored half q & 1. B region: N atom
-  // q >> 5 = 8r + tid / 32, K atom (q >> 4) & 1, row (q >> 1) & 7. The global
-  // half a lane fetches is the stored half XOR the row's swap bit.
-  const int a_j = (tid >> 5) & 1, a_m = (tid >> 1) & 15, a_h = (tid & 1) ^ swz_a(a_m);
-  const int b_i = tid >> 5, b_j = (tid >> 4) & 1, b_r = (tid >> 1) & 7;
-  const int b_h = (tid & 1) ^ swz_b(b_i & 1, b_r);
+  // Wave w loads A fragments f = 8r + w (row block f / 2, K atom f % 2 = w % 2)
+  // and B fragments likewise. Lane l of an A fragment fetches row l % 16 of M
+  // atom 2 * (f / 2) + (l / 16) % 2, half l / 32; lane l of a B fragment
+  // fetches row l % 8 of N atom 4 * (f / 2) + (l / 8) % 4, half l / 32.
+  const int kj = wave & 1;
   const int64_t a_row_bytes = K_rep * 512, b_row_bytes = K_rep * 256;
   const int64_t a_left = (p.M_rep - m_atom0) * a_row_bytes;
   const int64_t b_left = (p.N_rep - n_atom0) * b_row_bytes;
@@ -135,62 +153,73 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
       int(b_left < kOutOfRange ? b_left : kOutOfRange), kBufferFlags);
   uint32_t a_voff[kLoadsA], b_voff[kLoadsB];
 #pragma unroll
-  for (int r = 0; r < kLoadsA; ++r)
-    a_voff[r] = uint32_t((4 * r + wave) * a_row_bytes + a_j * 512 + a_m * 32 + a_h * 16);
+  for (int r = 0; r < kLoadsA; ++r) {
+    const int blk = (kWaves * r + wave) >> 1;
+    a_voff[r] = uint32_t((2 * blk + ((lane >> 4) & 1)) * a_row_bytes + kj * 512 +
+                         (lane & 15) * 32 + (lane >> 5) * 16);
+  }
 #pragma unroll
-  for (int r = 0; r < kLoadsB; ++r)
-    b_voff[r] = uint32_t((8 * r + b_i) * b_row_bytes + b_j * 256 + b_r * 32 + b_h * 16);
+  for (int r = 0; r < kLoadsB; ++r) {
+    const int blk = (kWaves * r + wave) >> 1;
+    b_voff[r] = uint32_t((4 * blk + ((lane >> 3) & 3)) * b_row_bytes + kj * 256 +
+                         (lane & 7) * 32 + (lane >> 5) * 16);
+  }
 
   // Loads of slab k into stage st (slabs past K_rep, and K atoms past it, read 0).
   auto issue = [&](Stage& st, int64_t k) {
     const uint32_t koff_a = uint32_t(k * kSlabKAtoms * 512), koff_b = uint32_t(k * kSlabKAtoms * 256);
-    const bool a_k = k * kSlabKAtoms + a_j < K_rep, b_k = k * kSlabKAtoms + b_j < K_rep;
+    const bool k_ok = k * kSlabKAtoms + kj < K_rep;
 #pragma unroll
     for (int r = 0; r < kLoadsA; ++r)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          a_rsrc, (__attribute__((address_space(3))) void*)&st.a[r * kThreads + wave * kWave], 16,
-          a_k ? a_voff[r] : kOutOfRange, koff_a, 0, 0);
+          a_rsrc, (__attribute__((address_space(3))) void*)&st.a[kWaves * r + wave][0], 16,
+          k_ok ? a_voff[r] : kOutOfRange, koff_a, 0, 0);
 #pragma unroll
     for (int r = 0; r < kLoadsB; ++r)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          b_rsrc, (__attribute__((address_space(3))) void*)&st.b[r * kThreads + wave * kWave], 16,
-          b_k ? b_voff[r] : kOutOfRange, koff_b, 0, 0);
+          b_rsrc, (__attribute__((address_space(3))) void*)&st.b[kWaves * r + wave][0], 16,
+          k_ok ? b_voff[r] : kOutOfRange, koff_b, 0, 0);
   };
 
-  // ---- per-lane fragment offsets (bytes) in a stage region ----
-  const int m = lane & 15, g = lane >> 4;
-  const int a_frag = (wm * 8) * 1024 + (g >> 1) * 512 + m * 32 + 16 * ((g & 1) ^ swz_a(m));
-  const int nb_atom = m >> 3, rr = m & 7;  // B row n = lane % 16 -> atom parity, row in atom
-  const int b_frag = (wn * 8) * 1024 + nb_atom * 512 + (g >> 1) * 256 + rr * 32 +
-                     16 * ((g & 1) ^ swz_b(nb_atom, rr));
-
   // ---- accumulators: C (read once, here) or the scalar ----
-  f32x4 acc[8][8];
-  const int64_t d_row_atom0 = m_atom0 + wm * 8;
-  const int64_t d_col_atom0 = n_atom0 + wn * 16 + (g >> 1);
+  // Block (pm, qn) of the wave: rows 32 * (4 wm + pm) .. +31, columns
+  // 32 * (2 wn + qn) .. +31 of the tile. Lane l, register 4q + t: row l % 32,
+  // column 8q + 4 (l / 32) + t of the block.
+  f32x16 acc[kWaveBlocksM][kWaveBlocksN];
+  const int64_t lane_row_atom = m_atom0 + 2 * (kWaveBlocksM * wm) + ((lane >> 4) & 1);  // + 2 pm
+  const int64_t lane_col_atom = n_atom0 + 4 * (kWaveBlocksN * wn);                     // + 4 qn + q
   const bool interior = m_atom0 + kTileMAtoms <= p.M_rep && n_atom0 + kTileNAtoms <= p.N_rep;
-  const int64_t d_lane = (((tc.b * p.M_rep + d_row_atom0) * p.N_rep + d_col_atom0) * 16 + m) * 8 +
-                         4 * (g & 1);
+  const int64_t d_lane =
+      (((tc.b * p.M_rep + lane_row_atom) * p.N_rep + lane_col_atom) * 16 + (lane & 15)) * 8 +
+      4 * (lane >> 5);
   const int64_t d_mstride = p.N_rep * kAtomFloats;  // next M atom
   if constexpr (kHasC) {
     // Blocks outside a ragged last tile read a clamped (valid) address: their
     // accumulators are never stored, and one branch-free path keeps the 256
     // accumulator registers in place.
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+    for (int pm = 0; pm < kWaveBlocksM; ++pm)
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const int64_t ma = d_row_atom0 + mb < p.M_rep ? d_row_atom0 + mb : p.M_rep - 1;
-        const int64_t na = d_col_atom0 + 2 * nb < p.N_rep ? d_col_atom0 + 2 * nb : p.N_rep - 1;
-        acc[mb][nb] = load16f(p.C + (((tc.b * p.M_rep + ma) * p.N_rep + na) * 16 + m) * 8 +
-                              4 * (g & 1));
-      }
+      for (int qn = 0; qn < kWaveBlocksN; ++qn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t ra = lane_row_atom + 2 * pm, ca = lane_col_atom + 4 * qn + q;
+          const int64_t ma = ra < p.M_rep ? ra : p.M_rep - 1;
+          const int64_t na = ca < p.N_rep ? ca : p.N_rep - 1;
+          const f32x4 v = load16f(p.C + (((tc.b * p.M_rep + ma) * p.N_rep + na) * 16 +
+                                         (lane & 15)) * 8 + 4 * (lane >> 5));
+          acc[pm][qn][4 * q + 0] = v[0];
+          acc[pm][qn][4 * q + 1] = v[1];
+          acc[pm][qn][4 * q + 2] = v[2];
+          acc[pm][qn][4 * q + 3] = v[3];
+        }
   } else {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+    for (int pm = 0; pm < kWaveBlocksM; ++pm)
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
-        acc[mb][nb] = f32x4{p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
+      for (int qn = 0; qn < kWaveBlocksN; ++qn)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[pm][qn][e] = p.c_scalar;
   }
 
   // Slabs 0..3 into the ring; C (issued first) and slab 0 must have landed.
@@ -203,35 +232,38 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
 
-  u32x4 bf[2][8], af[2][8];
-  // Fragment reads are volatile so that they stay where they are written
-  // (issued a half slab ahead of their MFMAs) instead of being sunk to their
-  // first use.
-  auto read_frags = [&](const Stage& st, u32x4 (&b)[8], u32x4 (&a)[8]) {
-    const lds_cchar* sa = (const lds_cchar*)(st.a);
-    const lds_cchar* sb = (const lds_cchar*)(st.b);
+  // Fragments of one slab: [K atom][block]. Reads are volatile LDS loads so
+  // they stay where they are written (a half slab ahead of their MFMAs)
+  // instead of being sunk to their first use.
+  using FragB = u32x4[2][kWaveBlocksN];
+  using FragA = u32x4[2][kWaveBlocksM];
+  FragB fb[2];
+  FragA fa[2];
+  auto read_frags = [&](const Stage& st, FragB& b, FragA& a) {
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-      b[nb] = *reinterpret_cast<const volatile lds_u32x4*>(sb + b_frag + nb * 1024);
+    for (int j = 0; j < 2; ++j) {
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-      a[mb] = *reinterpret_cast<const volatile lds_u32x4*>(sa + a_frag + mb * 1024);
+      for (int i = 0; i < kWaveBlocksN; ++i)
+        b[j][i] = *(const volatile lds_u32x4*)&st.b[2 * (kWaveBlocksN * wn + i) + j][lane];
+#pragma unroll
+      for (int i = 0; i < kWaveBlocksM; ++i)
+        a[j][i] = *(const volatile lds_u32x4*)&st.a[2 * (kWaveBlocksM * wm + i) + j][lane];
+    }
   };
-  auto mfma_rows = [&](const u32x4 (&b)[8], const u32x4 (&a)[8], int mb0) {
+  auto mfma_katom = [&](const u32x4 (&b)[kWaveBlocksN], const u32x4 (&a)[kWaveBlocksM]) {
 #pragma unroll
-    for (int mb = mb0; mb < mb0 + 4; ++mb)
+    for (int pm = 0; pm < kWaveBlocksM; ++pm)
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) acc[mb][nb] = mfma_16x16x32<DT>(b[nb], a[mb], acc[mb][nb]);
+      for (int qn = 0; qn < kWaveBlocksN; ++qn)
+        acc[pm][qn] = mfma_32x32x16<DT>(b[qn], a[pm], acc[pm][qn]);
   };
 
-  read_frags(st0, bf[0], af[0]);
+  read_frags(st0, fb[0], fa[0]);
 
-  // One slab: its fragments are in registers set F; `cur` is its stage,
-  // `nxt` the next slab's.
-  auto slab = [&](int64_t s, Stage& cur, const Stage& nxt, u32x4 (&bc)[8], u32x4 (&ac)[8],
-                  u32x4 (&bn)[8], u32x4 (&an)[8]) {
+  auto slab = [&](int64_t s, Stage& cur, const Stage& nxt, FragB& bc, FragA& ac, FragB& bn,
+                  FragA& an) {
     __builtin_amdgcn_sched_barrier(0);
-    mfma_rows(bc, ac, 0);
+    mfma_katom(bc[0], ac[0]);
     // own loads of slab s+1 landed (slabs s+2, s+3 may still be in flight);
     // own fragment reads of this stage done
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsPerSlab, 0));
@@ -240,42 +272,40 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
     asm volatile("" ::: "memory");
     issue(cur, s + kStages);
     read_frags(nxt, bn, an);
-    mfma_rows(bc, ac, 4);
-    // order after the barrier: the next slab's 16 fragment reads first, then
-    // the 32 MFMAs with the 8 loads of slab s+4 spread among them
-    __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+    mfma_katom(bc[1], ac[1]);
+    // order after the barrier: the next slab's fragment reads first, then
+    // the MFMAs with the loads of slab s+4 spread among them
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kWaveBlocksM + kWaveBlocksN), 0);
 #pragma unroll
     for (int i = 0; i < kLoadsPerSlab; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, kWaveBlocksM * kWaveBlocksN - kLoadsPerSlab, 0);
   };
   const int64_t n_slabs = (K_rep + kSlabKAtoms - 1) / kSlabKAtoms;
   for (int64_t s = 0; s < n_slabs; s += kStages) {
-    slab(s + 0, st0, st1, bf[0], af[0], bf[1], af[1]);
-    slab(s + 1, st1, st2, bf[1], af[1], bf[0], af[0]);
-    slab(s + 2, st2, st3, bf[0], af[0], bf[1], af[1]);
-    slab(s + 3, st3, st0, bf[1], af[1], bf[0], af[0]);
+    slab(s + 0, st0, st1, fb[0], fa[0], fb[1], fa[1]);
+    slab(s + 1, st1, st2, fb[1], fa[1], fb[0], fa[0]);
+    slab(s + 2, st2, st3, fb[0], fa[0], fb[1], fa[1]);
+    slab(s + 3, st3, st0, fb[1], fa[1], fb[0], fa[0]);
   }
   // No load may still be writing LDS when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-  // ---- epilogue: 16-byte stores, one 1 KB contiguous block per MFMA block ----
-  if (interior) {
+  // ---- epilogue: per block, four 16-byte stores (one per N atom) ----
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+  for (int pm = 0; pm < kWaveBlocksM; ++pm)
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
-        store16f(p.D + d_lane + mb * d_mstride + nb * 2 * kAtomFloats, acc[mb][nb]);
-  } else {
+    for (int qn = 0; qn < kWaveBlocksN; ++qn)
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
-        if (d_row_atom0 + mb < p.M_rep && d_col_atom0 + 2 * nb < p.N_rep)
-          store16f(p.D + d_lane + mb * d_mstride + nb * 2 * kAtomFloats, acc[mb][nb]);
-  }
+      for (int q = 0; q < 4; ++q) {
+        const f32x4 v = {acc[pm][qn][4 * q + 0], acc[pm][qn][4 * q + 1], acc[pm][qn][4 * q + 2],
+                         acc[pm][qn][4 * q + 3]};
+        float* dst = p.D + d_lane + 2 * pm * d_mstride + (4 * qn + q) * kAtomFloats;
+        if (interior || (lane_row_atom + 2 * pm < p.M_rep && lane_col_atom + 4 * qn + q < p.N_rep))
+          store16f(dst, v);
+      }
 }
 
 }  // namespace
