@@ -99,6 +99,9 @@ def main():
     ap.add_argument("--kernel", default="auto", choices=["auto", "direct", "tiled", "skinny"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kmajor", action="store_true",
+                    help="A and B are stored K-major (transposed) in HBM; the step packs them "
+                         "with pack_operand_kmajor")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -121,6 +124,10 @@ def main():
     inp = workloads.make_inputs(w, seed=0)
     a = torch.from_numpy(inp["a"].view(np.int16)).to(dev)
     b = torch.from_numpy(inp["b"].view(np.int16)).to(dev)
+    if args.kmajor:   # store the operands transposed: element (row, k) at [b, k, row]
+        a = a.transpose(1, 2).contiguous()
+        b = b.transpose(1, 2).contiguous()
+    pack = bmm.pack_operand_kmajor if args.kmajor else bmm.pack_operand
     C = None if inp["c_tensor"] is None else torch.from_numpy(inp["c_tensor"]).to(dev)
     c = float(inp["c_scalar"])
     A = torch.empty((w.batch, w.M_rep, w.K_rep, 16, 8), dtype=torch.int32, device=dev)
@@ -133,10 +140,10 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        bmm.pack_operand(a, 16, out=A)
+        pack(a, 16, out=A)
         if ev is not None:
             ev[1].record(stream)
-        bmm.pack_operand(b, 8, out=B)
+        pack(b, 8, out=B)
         if ev is not None:
             ev[2].record(stream)
         bmm.mma_tile(A, B, C, c, w.dtype, out=D, kernel=kernel)
@@ -199,7 +206,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
                    "c": "tensor" if w.c_tensor else "scalar", "kernel": kernel,
-                   "step": "pack A + pack B + mma_tile"},
+                   "step": ("pack_kmajor A + pack_kmajor B + mma_tile" if args.kmajor
+                            else "pack A + pack B + mma_tile")},
         "roofline": roofline,
         "kernels": {"pack_a_us": round(pa.mean() * 1e3, 2), "pack_b_us": round(pb.mean() * 1e3, 2),
                     "mma_tile_us": round(mm.mean() * 1e3, 2),

@@ -21,7 +21,7 @@ import os
 
 import torch
 
-__all__ = ["BmmError", "pack_operand", "box_copy", "mma_tile", "select_kernel",
+__all__ = ["BmmError", "pack_operand", "pack_operand_kmajor", "box_copy", "mma_tile", "select_kernel",
            "library_path", "KERNELS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,13 +75,14 @@ def lib():
         L.bmm_abi_version.restype = ctypes.c_int
         L.bmm_last_error.restype = ctypes.c_char_p
         L.bmm_pack_operand.argtypes = [p, p, i64, i64, i64, i64, i32, p]
+        L.bmm_pack_operand_kmajor.argtypes = [p, p, i64, i64, i64, i64, i32, p]
         L.bmm_box_copy.argtypes = [p, p, ctypes.POINTER(BoxDesc), ctypes.POINTER(i64), p]
         L.bmm_mma_tile.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64, i64, ctypes.c_int,
                                    p]
         L.bmm_mma_tile_with.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64, i64,
                                         ctypes.c_int, i32, p]
         L.bmm_select_kernel.argtypes = [i64, i64, i64, i64]
-        for f in (L.bmm_pack_operand, L.bmm_box_copy, L.bmm_mma_tile, L.bmm_mma_tile_with,
+        for f in (L.bmm_pack_operand, L.bmm_pack_operand_kmajor, L.bmm_box_copy, L.bmm_mma_tile, L.bmm_mma_tile_with,
                   L.bmm_select_kernel):
             f.restype = ctypes.c_int
         _lib = L
@@ -134,6 +135,31 @@ def pack_operand(x: torch.Tensor, atom_rows: int, K: int | None = None,
         raise ValueError(f"pack_operand: out must be a contiguous 32-bit tensor of shape {shape}")
     _check(lib().bmm_pack_operand(_ptr(out), _ptr(x), batch, rows, K, ld, atom_rows,
                                   _stream(x)))
+    return out
+
+
+def pack_operand_kmajor(xt: torch.Tensor, atom_rows: int, rows: int | None = None,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    """K-major (batch, K, ld) or (K, ld) 16-bit tensor holding element (row, k)
+    at [b, k, row] -> packed words (batch, rows/R, K/16, R, 8) int32, the same
+    words pack_operand gives for the row-major matrix. rows defaults to ld."""
+    _require_cuda(xt)
+    if xt.element_size() != 2:
+        raise ValueError("pack_operand_kmajor takes 16-bit (f16/bf16 bit) tensors")
+    if xt.dim() == 2:
+        xt = xt.unsqueeze(0)
+    batch, K, ld = xt.shape
+    if xt.stride(2) != 1 or (K > 1 and xt.stride(1) != ld) or \
+            (batch > 1 and xt.stride(0) != K * ld):
+        raise ValueError("pack_operand_kmajor: source must be (batch, K, ld) with dense strides")
+    rows = ld if rows is None else rows
+    shape = (batch, rows // atom_rows, K // 16, atom_rows, 8)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.int32, device=xt.device)
+    elif tuple(out.shape) != shape or not out.is_contiguous() or out.element_size() != 4:
+        raise ValueError(f"pack_operand_kmajor: out must be a contiguous 32-bit tensor of shape {shape}")
+    _check(lib().bmm_pack_operand_kmajor(_ptr(out), _ptr(xt), batch, rows, K, ld, atom_rows,
+                                         _stream(xt)))
     return out
 
 

@@ -53,6 +53,16 @@ int bmm_pack_operand(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t 
                     "pack_operand launch");
 }
 
+int bmm_pack_operand_kmajor(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
+                            int64_t K, int64_t ld_src, int32_t atom_rows, void* stream) {
+  bmm::Status st = bmm::check_pack_kmajor(dst, src, batch, rows, K, ld_src, atom_rows);
+  if (!st.ok()) return report(st);
+  if (batch == 0 || rows == 0 || K == 0) return report(st);
+  return hip_status(bmm::launch_pack_kmajor(dst, src, batch, rows, K, ld_src, atom_rows,
+                                            static_cast<hipStream_t>(stream)),
+                    "pack_operand_kmajor launch");
+}
+
 int bmm_box_copy(void* dst_image, const void* src, const bmm_box_desc* desc,
                  int64_t* bytes_moved, void* stream) {
   bmm::Status st = bmm::check_box(dst_image, src, desc);

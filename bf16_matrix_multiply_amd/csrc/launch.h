@@ -20,6 +20,8 @@ struct MmaArgs {
 
 hipError_t launch_pack(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
                        int64_t K, int64_t ld, int R, hipStream_t s);
+hipError_t launch_pack_kmajor(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
+                              int64_t K, int64_t ld, int R, hipStream_t s);
 hipError_t launch_box(void* dst, const void* src, const bmm_box_desc& d, hipStream_t s);
 hipError_t launch_mma_direct(const MmaArgs& a, hipStream_t s);
 // The tiled kernel addresses one tile's operands with 32-bit buffer offsets:

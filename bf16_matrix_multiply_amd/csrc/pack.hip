@@ -1,4 +1,4 @@
-// Row-major halves -> packed b32 atoms (the operand layouts of the mma.sync
+// Row-major (or K-major) halves -> packed b32 atoms (the operand layouts of the mma.sync
 // page, "Operand coordinates and ownership", built from row-major matrices as
 // in the page's worked example).
 //
@@ -45,7 +45,66 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(uint32_t* __restrict
   }
 }
 
+// ---- K-major sources ----
+// The source holds the transpose: element (row, k) at src[b, k, row], rows
+// contiguous. One workgroup turns a 64-row x 64-K tile around through LDS:
+// lanes read 16-byte pieces of source rows (8 consecutive rows at one k,
+// coalesced), a barrier, then each lane gathers the 8 consecutive K values of
+// one row from the tile and stores them as one 16-byte packed chunk, the
+// chunks of the tile in destination order (contiguous stores).
+constexpr int kTile = 64;
+constexpr int kTilePitch = kTile + 8;  // u16 per LDS row (16-byte aligned rows)
+
+template <int R>
+__global__ __launch_bounds__(256) void pack_kmajor_kernel(uint32_t* __restrict__ dst,
+                                                          const uint16_t* __restrict__ src,
+                                                          int64_t rows, int64_t K, int64_t ld) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile][kTilePitch];
+  const int tid = threadIdx.x;
+  const int64_t row0 = int64_t(blockIdx.x) * kTile, k0 = int64_t(blockIdx.y) * kTile;
+  const int64_t b = blockIdx.z;
+  const uint16_t* sb = src + b * K * ld;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = tid + 256 * u;
+    const int kk = c >> 3, rc = (c & 7) * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (k0 + kk < K && row0 + rc < rows)
+      v = load16_nt(reinterpret_cast<const uint32_t*>(sb + (k0 + kk) * ld + row0 + rc));
+    *reinterpret_cast<u32x4*>(&tile[kk][rc]) = v;
+  }
+  __syncthreads();
+  constexpr int kLog2R = R == 16 ? 4 : 3;
+  const int64_t rows_rep = rows / R, K_rep = K / 16;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int c = tid + 256 * u;
+    // chunk c of the tile: row block c / (8R), then K atom, row in atom, half
+    const int rb = c >> (kLog2R + 3), rem = c & (8 * R - 1);
+    const int kr = rem >> (kLog2R + 1), i = (rem >> 1) & (R - 1), h = rem & 1;
+    const int row_l = rb * R + i, k_l = kr * 16 + h * 8;
+    if (row0 + row_l >= rows || k0 + k_l >= K) continue;
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = uint32_t(tile[k_l + 2 * e][row_l]) | (uint32_t(tile[k_l + 2 * e + 1][row_l]) << 16);
+    const int64_t off = (((b * rows_rep + row0 / R + rb) * K_rep + k0 / 16 + kr) * R + i) * 8 + 4 * h;
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst + off));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pack_kmajor(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
+                              int64_t K, int64_t ld, int R, hipStream_t s) {
+  const dim3 grid(unsigned((rows + kTile - 1) / kTile), unsigned((K + kTile - 1) / kTile),
+                  unsigned(batch));
+  if (R == 16)
+    hipLaunchKernelGGL(pack_kmajor_kernel<16>, grid, dim3(256), 0, s, dst, src, rows, K, ld);
+  else
+    hipLaunchKernelGGL(pack_kmajor_kernel<8>, grid, dim3(256), 0, s, dst, src, rows, K, ld);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
                        int64_t K, int64_t ld, int R, hipStream_t s) {

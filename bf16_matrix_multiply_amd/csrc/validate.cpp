@@ -70,6 +70,39 @@ Status check_pack(const uint32_t* dst, const uint16_t* src, int64_t batch, int64
   return Status{};
 }
 
+Status check_pack_kmajor(const uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
+                         int64_t K, int64_t ld_src, int32_t atom_rows) {
+  if (atom_rows != 16 && atom_rows != 8)
+    return fail(BMM_EINVAL, "pack_operand_kmajor: atom_rows must be 16 (A) or 8 (B), got %lld",
+                atom_rows);
+  if (batch < 0 || rows < 0 || K < 0)
+    return fail(BMM_EINVAL, "pack_operand_kmajor: negative extent");
+  if (batch > 65535 || rows > kMaxExtent || K > (int64_t(1) << 22))
+    return fail(BMM_EINVAL, "pack_operand_kmajor: extent too large (batch <= 65535, K <= 2^22)");
+  if (rows % atom_rows)
+    return fail(BMM_EINVAL,
+                "pack_operand_kmajor: rows (%lld) is not a multiple of atom_rows (%lld)", rows,
+                atom_rows);
+  if (K % 16) return fail(BMM_EINVAL, "pack_operand_kmajor: K (%lld) is not a multiple of 16", K);
+  if (ld_src < rows)
+    return fail(BMM_EINVAL, "pack_operand_kmajor: ld_src (%lld) < rows (%lld)", ld_src, rows);
+  if (ld_src > (int64_t(1) << 32)) return fail(BMM_EINVAL, "pack_operand_kmajor: ld_src too large");
+  if (batch == 0 || rows == 0 || K == 0) return Status{};
+  if (!dst || !src) return fail(BMM_EINVAL, "pack_operand_kmajor: null pointer");
+  if (ld_src % 8)
+    return fail(BMM_EALIGN, "pack_operand_kmajor: ld_src (%lld) must be a multiple of 8 elements",
+                ld_src);
+  if (!aligned16(dst) || !aligned16(src))
+    return fail(BMM_EALIGN, "pack_operand_kmajor: dst and src must be 16-byte aligned");
+  int64_t dst_bytes = mul_capped({batch, rows, K, 2});
+  int64_t src_bytes = mul_capped({batch * K - 1, ld_src, 2});
+  if (dst_bytes < 0 || src_bytes < 0) return fail(BMM_EINVAL, "pack_operand_kmajor: too large");
+  src_bytes += rows * 2;
+  if (overlaps(dst, dst_bytes, src, src_bytes))
+    return fail(BMM_EOVERLAP, "pack_operand_kmajor: dst overlaps src");
+  return Status{};
+}
+
 Status check_box(const void* dst, const void* src, const bmm_box_desc* d) {
   if (!d) return fail(BMM_EINVAL, "box_copy: null descriptor");
   if (d->rank < 1 || d->rank > 5) return fail(BMM_EINVAL, "box_copy: rank %lld not in 1..5", d->rank);

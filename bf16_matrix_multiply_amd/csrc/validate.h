@@ -18,6 +18,9 @@ struct Status {
 Status check_pack(const uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
                   int64_t K, int64_t ld_src, int32_t atom_rows);
 
+Status check_pack_kmajor(const uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
+                         int64_t K, int64_t ld_src, int32_t atom_rows);
+
 Status check_box(const void* dst, const void* src, const bmm_box_desc* d);
 
 Status check_mma(const float* D, const uint32_t* A, const uint32_t* B, const float* C,

@@ -77,6 +77,28 @@ int bmm_pack_operand(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t 
                      int64_t K, int64_t ld_src, int32_t atom_rows, void* stream);
 
 /*
+ * bmm_pack_operand_kmajor — packing from a K-major (transposed) source.
+ *
+ * The mma.sync page ("Accumulation, transpose and alpha/beta") leaves a
+ * logical transpose to explicit preparation: a view cannot move values
+ * between lanes, so an operand whose K values are not contiguous must be
+ * rewritten. This is that preparation for the packed layouts: the source
+ * holds element (row, k) of the logical operand at src[b, k, row] (rows
+ * contiguous), and the result is exactly what bmm_pack_operand gives for the
+ * row-major matrix:
+ *
+ *   dst[b, r, kr, i, w] = src[b, 16*kr+2*w, R*r+i] | src[b, 16*kr+2*w+1, R*r+i] << 16
+ *
+ * dst       (batch, rows/R, K/16, R, 8) uint32, contiguous, 16-byte aligned.
+ * src       (batch, K, ld_src) 16-bit values, batch stride K*ld_src, 16-byte aligned.
+ * rows      multiple of atom_rows; K multiple of 16 and at most 2^22; ld_src >= rows and
+ *           a multiple of 8; batch at most 65535. Zero batch, rows or K is a no-op.
+ * Errors: as bmm_pack_operand.
+ */
+int bmm_pack_operand_kmajor(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
+                            int64_t K, int64_t ld_src, int32_t atom_rows, void* stream);
+
+/*
  * bmm_box_copy — a rectangular global box through an LDS image.
  *
  * The role of the TMA tile-mode box load on the cp.async.bulk.tensor page

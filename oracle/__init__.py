@@ -51,6 +51,7 @@ class Oracle:
         L.oracle_h2f_array.argtypes = [p, p, i64, ctypes.c_int]
         L.oracle_pack.argtypes = [p, p, i64, i64, i64, i64, i64]
         L.oracle_unpack.argtypes = [p, p, i64, i64, i64, i64]
+        L.oracle_pack_kmajor.argtypes = [p, p, i64, i64, i64, i64, i64]
         L.oracle_mma.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64, i64, ctypes.c_int]
         L.oracle_mma_sampled.argtypes = [p, p, i64, p, p, p, ctypes.c_float, i64, i64, i64,
                                          i64, ctypes.c_int]
@@ -81,6 +82,20 @@ class Oracle:
         rc = self.L.oracle_pack(_ptr(out), _ptr(x), batch, rows, K, ld, atom_rows)
         if rc != 0:
             raise ValueError("oracle_pack rejected its arguments")
+        return out
+
+    def pack_kmajor(self, x: np.ndarray, atom_rows: int, rows: int | None = None) -> np.ndarray:
+        """K-major (batch, K, ld) uint16 (element (row, k) at [b, k, row]) ->
+        (batch, rows/R, K/16, R, 8) uint32 words; rows defaults to ld."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        if x.ndim == 2:
+            x = x[None]
+        batch, K, ld = x.shape
+        rows = ld if rows is None else rows
+        out = np.empty((batch, rows // atom_rows, K // 16, atom_rows, 8), np.uint32)
+        rc = self.L.oracle_pack_kmajor(_ptr(out), _ptr(x), batch, rows, K, ld, atom_rows)
+        if rc != 0:
+            raise ValueError("oracle_pack_kmajor rejected its arguments")
         return out
 
     def unpack(self, p: np.ndarray, atom_rows: int) -> np.ndarray:
@@ -203,6 +218,10 @@ def pack(x, atom_rows, K=None):
 
 def unpack(p, atom_rows):
     return default().unpack(p, atom_rows)
+
+
+def pack_kmajor(x, atom_rows, rows=None):
+    return default().pack_kmajor(x, atom_rows, rows)
 
 
 def mma(A, B, C, c, dtype):

@@ -106,6 +106,28 @@ int oracle_pack(uint32_t* P, const uint16_t* X, int64_t batch, int64_t rows, int
   return 0;
 }
 
+/* Packing from a K-major source: X is (batch, K, ld) with X[b, k, row] the
+ * logical element (row, k) (the transpose of the row-major case), batch
+ * stride K*ld. Same packed result as oracle_pack of the logical matrix:
+ *   P[b, r, kr, i, w] = X[b, 16*kr+2*w, R*r+i] | X[b, 16*kr+2*w+1, R*r+i] << 16
+ */
+int oracle_pack_kmajor(uint32_t* P, const uint16_t* X, int64_t batch, int64_t rows, int64_t K,
+                       int64_t ld, int64_t R) {
+  if ((R != 16 && R != 8) || rows % R || K % 16 || ld < rows) return -1;
+  const int64_t rows_rep = rows / R, K_rep = K / 16;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t r = 0; r < rows_rep; ++r)
+      for (int64_t kr = 0; kr < K_rep; ++kr)
+        for (int64_t i = 0; i < R; ++i)
+          for (int64_t w = 0; w < 8; ++w) {
+            const uint16_t* col = X + b * K * ld + (R * r + i);
+            uint32_t lo = col[(16 * kr + 2 * w) * ld];
+            uint32_t hi = col[(16 * kr + 2 * w + 1) * ld];
+            P[(((b * rows_rep + r) * K_rep + kr) * R + i) * 8 + w] = lo | (hi << 16);
+          }
+  return 0;
+}
+
 /* Inverse of oracle_pack into a dense (batch, rows, K) array. */
 int oracle_unpack(uint16_t* X, const uint32_t* P, int64_t batch, int64_t rows, int64_t K,
                   int64_t R) {

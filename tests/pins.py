@@ -58,6 +58,26 @@ def pin_pack_arange(o):
         assert np.array_equal(P[0], xv | ((xv + 1) << 16)), (R, rows, K)
 
 
+def pin_pack_kmajor(o):
+    """K-major packer == numpy transpose followed by the row-major packer
+    (pinned above), and the arange closed form read through the transpose;
+    several atom counts, both atom heights, batch 2, ld > rows."""
+    rng = np.random.default_rng(8)
+    for R, rows, K, ld in ((16, 48, 64, 48), (8, 40, 96, 56), (16, 16, 16, 24)):
+        xt = util.random_bits(rng, (2, K, ld))                      # [b, k, row]
+        logical = np.ascontiguousarray(xt[:, :, :rows].transpose(0, 2, 1))
+        assert np.array_equal(o.pack_kmajor(xt, R, rows), util.page_recipe_pack(logical, R)), \
+            (R, rows, K, ld)
+    R, rows, K = 8, 24, 32
+    xt = np.arange(K * rows, dtype=np.uint32).astype(np.uint16).reshape(1, K, rows)
+    P = o.pack_kmajor(xt, R)
+    r, kr, i, w = np.meshgrid(np.arange(rows // R), np.arange(K // 16), np.arange(R),
+                              np.arange(8), indexing="ij")
+    lo = ((16 * kr + 2 * w) * rows + R * r + i).astype(np.uint32)
+    hi = ((16 * kr + 2 * w + 1) * rows + R * r + i).astype(np.uint32)
+    assert np.array_equal(P[0], lo | (hi << 16))
+
+
 def pin_roundtrip(o):
     """unpack(pack(x)) == x on all 65536 bit patterns (NaN encodings included),
     for both atom heights: the packer moves bits, never values."""

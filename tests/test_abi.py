@@ -166,3 +166,29 @@ def test_select_kernel(L):
     for shape in [(1, 1, 1, 2), (1, 8, 16, 16), (1, 256, 512, 256), (1, 1, 2048, 1024),
                   (1, 512, 1024, 512)]:
         assert L.bmm_select_kernel(*shape) in (1, 2, 3)
+
+
+def pack_km(L, dst=P0, src=P1, batch=1, rows=16, K=32, ld=16, R=16):
+    return L.bmm_pack_operand_kmajor(dst, src, batch, rows, K, ld, R, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(R=4), EINVAL, "atom_rows"),
+    (dict(rows=24, ld=24, R=16), EINVAL, "multiple of atom_rows"),
+    (dict(K=40), EINVAL, "multiple of 16"),
+    (dict(ld=8), EINVAL, "ld_src"),
+    (dict(ld=20), EALIGN, "multiple of 8"),
+    (dict(batch=70000), EINVAL, "too large"),
+    (dict(K=(1 << 22) + 16), EINVAL, "too large"),
+    (dict(dst=P0 + 4), EALIGN, "aligned"),
+    (dict(dst=0), EINVAL, "null"),
+    (dict(dst=P1 + 32), EOVERLAP, "overlaps"),
+])
+def test_pack_kmajor_rejects(L, kw, code, needle):
+    assert pack_km(L, **kw) == code
+    assert needle in err(L)
+
+
+def test_pack_kmajor_empty_is_noop(L):
+    assert pack_km(L, dst=0, src=0, batch=0) == 0
+    assert pack_km(L, dst=0, src=0, K=0) == 0

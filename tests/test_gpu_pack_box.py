@@ -53,6 +53,41 @@ def test_pack_empty_and_errors():
     assert (sentinel == 7).all()
 
 
+@pytest.mark.parametrize("R", [16, 8])
+def test_pack_kmajor_all_bit_patterns(R):
+    """K-major source: every bit pattern lands where the oracle puts it."""
+    xt = np.arange(1 << 17, dtype=np.uint32).astype(np.uint16).reshape(2, 256, 256)
+    got = gu.host_u32(bmm.pack_operand_kmajor(gu.dev_u16(xt), R))
+    assert np.array_equal(got, oracle.pack_kmajor(xt, R))
+
+
+@pytest.mark.parametrize("R,rows,K,ld", [(16, 16, 16, 16), (8, 8, 32, 40), (16, 48, 80, 96),
+                                         (8, 200, 336, 208), (16, 272, 1040, 272),
+                                         (16, 64, 64, 64), (8, 72, 144, 80)])
+def test_pack_kmajor_shapes(R, rows, K, ld):
+    """Ragged 64x64 tiles in both directions, ld > rows, batch 3."""
+    rng = np.random.default_rng(rows * 7 + K)
+    xt = util.random_bits(rng, (3, K, ld))
+    got = gu.host_u32(bmm.pack_operand_kmajor(gu.dev_u16(xt), R, rows=rows))
+    assert np.array_equal(got, oracle.pack_kmajor(xt, R, rows))
+
+
+def test_pack_kmajor_equals_rowmajor_pack_full_size():
+    """At 8192x8192 (A) and 16384x16384 (B): packing the K-major copy gives
+    the same words as packing the row-major matrix, and the oracle's words."""
+    rng = np.random.default_rng(3)
+    for rows, K, R in ((8192, 8192, 16), (16384, 16384, 8)):
+        x = workloads.draw_operand(rng, "normal", (1, rows, K), "bf16")
+        xd = gu.dev_u16(x)
+        xtd = xd.transpose(1, 2).contiguous()
+        got = bmm.pack_operand_kmajor(xtd, R)
+        ref = bmm.pack_operand(xd, R)
+        assert torch.equal(got, ref), (rows, K)
+        if rows == 8192:
+            assert np.array_equal(gu.host_u32(got), oracle.pack(x, R))
+        del x, xd, xtd, got, ref
+
+
 def test_box_page_example():
     """Two 8x16 uint32 boxes at (0,0) and (8,0): the image read back is the
     16x16 input, 1024 bytes for the two boxes."""

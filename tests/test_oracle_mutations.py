@@ -10,11 +10,12 @@ from tests import pins
 
 MUTATIONS = {
     "pack_halves_swapped": (
-        "= lo | (hi << 16);", "= hi | (lo << 16);",
+        "row[16 * kr + 2 * w + 1];\n            P[(((b * rows_rep + r) * K_rep + kr) * R + i) * 8 + w] = lo | (hi << 16);",
+        "row[16 * kr + 2 * w + 1];\n            P[(((b * rows_rep + r) * K_rep + kr) * R + i) * 8 + w] = hi | (lo << 16);",
         ["pin_pack_page_recipe", "pin_pack_arange"]),
     "pack_rows_and_k_atoms_transposed": (
-        "P[(((b * rows_rep + r) * K_rep + kr) * R + i) * 8 + w]",
-        "P[(((b * rows_rep + r) * R + i) * K_rep + kr) * 8 + w]",
+        "row[16 * kr + 2 * w + 1];\n            P[(((b * rows_rep + r) * K_rep + kr) * R + i) * 8 + w]",
+        "row[16 * kr + 2 * w + 1];\n            P[(((b * rows_rep + r) * R + i) * K_rep + kr) * 8 + w]",
         ["pin_pack_page_recipe", "pin_pack_arange"]),
     "f16_exponent_bias_off_by_one": (
         "expo - 25)", "expo - 24)",
@@ -43,6 +44,10 @@ MUTATIONS = {
     "last_k_atom_dropped": (
         "k < 16 * K_rep; ++k) {\n    float a", "k < 16 * K_rep - 16; ++k) {\n    float a",
         ["pin_page_example", "pin_quarter_closed_form"]),
+    "kmajor_k_and_row_strides_swapped": (
+        "uint32_t lo = col[(16 * kr + 2 * w) * ld];\n            uint32_t hi = col[(16 * kr + 2 * w + 1) * ld];",
+        "uint32_t lo = col[(16 * kr + 2 * w) * ld];\n            uint32_t hi = col[(16 * kr + 2 * w) * ld + 1];",
+        ["pin_pack_kmajor"]),
     "box_fill_not_zero": (
         "memset(out, 0, (size_t)elem_bytes);", "memset(out, 0x5a, (size_t)elem_bytes);",
         ["pin_box_oob"]),
