@@ -52,10 +52,10 @@ def traffic_from_profiles(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, inp, D_gpu, seconds: float):
+def cpu_baseline(w, inp, D_gpu, seconds: float, alpha=None, beta=None):
     """The oracle, as it stands, on the first rows of D (all N columns), sized
     to take about ``seconds`` of CPU time; also checks those rows against the
-    GPU result."""
+    GPU result (for the alpha/beta form: alpha * product + beta * C)."""
     import oracle
     from_rows = w.batch == 1
     A = oracle.pack(inp["a"], 16)
@@ -77,7 +77,17 @@ def cpu_baseline(w, inp, D_gpu, seconds: float):
     flops = 2.0 * rows * w.N * w.K
     Dl = D_gpu.transpose(0, 1, 3, 2, 4).reshape(w.batch, w.M, w.N)
     got = Dl[idx[:, 0], idx[:, 1], idx[:, 2]]
-    if w.exact:
+    if alpha is not None or beta is not None:
+        al, be = (1.0 if alpha is None else alpha), (1.0 if beta is None else beta)
+        P = oracle.mma_sampled(A, B, None, 0.0, w.dtype, idx).astype(np.float64)
+        if C is None:
+            cv = np.full(len(idx), float(inp["c_scalar"]))
+        else:
+            cv = C.transpose(0, 1, 3, 2, 4).reshape(w.batch, w.M, w.N)[idx[:, 0], idx[:, 1], idx[:, 2]]
+        ref = al * P + be * cv
+        bnd = abs(al) * oracle.bound(A, B, None, 0.0, w.dtype, idx) + abs(be) * np.abs(cv)
+        ok = bool((np.abs(got.astype(np.float64) - ref) <= 1e-3 * bnd).all())
+    elif w.exact:
         ok = bool(np.array_equal(got, out))
     else:
         bnd = oracle.bound(A, B, C, inp["c_scalar"], w.dtype, idx)
@@ -99,6 +109,9 @@ def main():
     ap.add_argument("--kernel", default="auto", choices=["auto", "direct", "tiled", "skinny"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--alpha", type=float, default=None,
+                    help="run the alpha/beta form D = alpha*A*B^T + beta*C (scaling in the epilogue)")
+    ap.add_argument("--beta", type=float, default=None)
     ap.add_argument("--kmajor", action="store_true",
                     help="A and B are stored K-major (transposed) in HBM; the step packs them "
                          "with pack_operand_kmajor")
@@ -146,7 +159,7 @@ def main():
         pack(b, 8, out=B)
         if ev is not None:
             ev[2].record(stream)
-        bmm.mma_tile(A, B, C, c, w.dtype, out=D, kernel=kernel)
+        bmm.mma_tile(A, B, C, c, w.dtype, out=D, kernel=kernel, alpha=args.alpha, beta=args.beta)
         if ev is not None:
             ev[3].record(stream)
 
@@ -206,6 +219,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
                    "c": "tensor" if w.c_tensor else "scalar", "kernel": kernel,
+                   "alpha": args.alpha, "beta": args.beta,
                    "step": ("pack_kmajor A + pack_kmajor B + mma_tile" if args.kmajor
                             else "pack A + pack B + mma_tile")},
         "roofline": roofline,
@@ -219,7 +233,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample of the same workload")
-        line["cpu_baseline"] = cpu_baseline(w, inp, D.cpu().numpy(), args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, inp, D.cpu().numpy(), args.cpu_seconds, args.alpha,
+                                            args.beta)
     print(json.dumps(line), flush=True)
 
 

@@ -81,8 +81,10 @@ def lib():
                                    p]
         L.bmm_mma_tile_with.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64, i64,
                                         ctypes.c_int, i32, p]
+        L.bmm_mma_tile_scaled.argtypes = [p, p, p, p, ctypes.c_float, ctypes.c_float,
+                                          ctypes.c_float, i64, i64, i64, i64, ctypes.c_int, i32, p]
         L.bmm_select_kernel.argtypes = [i64, i64, i64, i64]
-        for f in (L.bmm_pack_operand, L.bmm_pack_operand_kmajor, L.bmm_box_copy, L.bmm_mma_tile, L.bmm_mma_tile_with,
+        for f in (L.bmm_pack_operand, L.bmm_pack_operand_kmajor, L.bmm_box_copy, L.bmm_mma_tile, L.bmm_mma_tile_with, L.bmm_mma_tile_scaled,
                   L.bmm_select_kernel):
             f.restype = ctypes.c_int
         _lib = L
@@ -195,11 +197,14 @@ def box_copy(src: torch.Tensor, box, coords, n_repeat: int = 1, coord_step=None,
 
 def mma_tile(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None,
              c: float = 0.0, dtype="bf16", out: torch.Tensor | None = None,
-             kernel: str = "auto") -> torch.Tensor:
+             kernel: str = "auto", alpha: float | None = None,
+             beta: float | None = None) -> torch.Tensor:
     """D = A * B^T + C over packed operands; returns D (batch, M/16, N/8, 16, 8).
 
     C is a float32 tensor in D's layout or None (then every element starts
-    from the scalar ``c``). ``out`` may be C itself (in place)."""
+    from the scalar ``c``). ``out`` may be C itself (in place). With alpha or
+    beta given, the alpha/beta form runs instead (bmm_mma_tile_scaled):
+    D = fma(alpha, A * B^T, beta * C), the product accumulated from zero."""
     _require_cuda(A, B, C, out)
     if A.dim() != 5 or B.dim() != 5 or A.shape[3:] != (16, 8) or B.shape[3:] != (8, 8):
         raise ValueError("mma_tile: A must be (batch, M_rep, K_rep, 16, 8) and B "
@@ -219,9 +224,15 @@ def mma_tile(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None,
         out = torch.empty(shape, dtype=torch.float32, device=A.device)
     elif tuple(out.shape) != shape or out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError(f"mma_tile: out must be a contiguous float32 tensor of shape {shape}")
-    _check(lib().bmm_mma_tile_with(_ptr(out), _ptr(A), _ptr(B), _ptr(C), float(c), batch,
-                                   M_rep, N_rep, K_rep, _DTYPES[dtype], KERNELS[kernel],
-                                   _stream(A)))
+    if alpha is None and beta is None:
+        _check(lib().bmm_mma_tile_with(_ptr(out), _ptr(A), _ptr(B), _ptr(C), float(c), batch,
+                                       M_rep, N_rep, K_rep, _DTYPES[dtype], KERNELS[kernel],
+                                       _stream(A)))
+    else:
+        _check(lib().bmm_mma_tile_scaled(
+            _ptr(out), _ptr(A), _ptr(B), _ptr(C), float(c), 1.0 if alpha is None else float(alpha),
+            1.0 if beta is None else float(beta), batch, M_rep, N_rep, K_rep, _DTYPES[dtype],
+            KERNELS[kernel], _stream(A)))
     return out
 
 

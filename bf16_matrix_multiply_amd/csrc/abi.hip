@@ -80,25 +80,42 @@ int bmm_select_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep
   return choose_kernel(batch, M_rep, N_rep, K_rep);
 }
 
-int bmm_mma_tile_with(float* D, const uint32_t* A, const uint32_t* B, const float* C,
-                      float c_scalar, int64_t batch, int64_t M_rep, int64_t N_rep,
-                      int64_t K_rep, bmm_dtype dtype, int32_t kernel, void* stream) {
-  bmm::Status st = bmm::check_mma(D, A, B, C, batch, M_rep, N_rep, K_rep, dtype, kernel);
+namespace {
+
+int mma_common(const bmm::MmaArgs& a0, int32_t kernel, void* stream) {
+  bmm::Status st = bmm::check_mma(a0.D, a0.A, a0.B, a0.C, a0.batch, a0.M_rep, a0.N_rep,
+                                  a0.K_rep, a0.dtype, kernel);
   if (!st.ok()) return report(st);
-  if (batch == 0 || M_rep == 0 || N_rep == 0) return report(st);
-  const bmm::MmaArgs a{D, A, B, C, c_scalar, batch, M_rep, N_rep, K_rep, int(dtype)};
-  if (kernel == BMM_KERNEL_AUTO) kernel = choose_kernel(batch, M_rep, N_rep, K_rep);
+  if (a0.batch == 0 || a0.M_rep == 0 || a0.N_rep == 0) return report(st);
+  if (kernel == BMM_KERNEL_AUTO) kernel = choose_kernel(a0.batch, a0.M_rep, a0.N_rep, a0.K_rep);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (kernel) {
-    case BMM_KERNEL_DIRECT: return hip_status(bmm::launch_mma_direct(a, s), "mma_tile direct launch");
+    case BMM_KERNEL_DIRECT: return hip_status(bmm::launch_mma_direct(a0, s), "mma_tile direct launch");
     case BMM_KERNEL_TILED:
-      if (K_rep >= bmm::kTiledMaxKRep) {
+      if (a0.K_rep >= bmm::kTiledMaxKRep) {
         g_last_error = "mma_tile: the tiled kernel takes K_rep < 262144";
         return BMM_EINVAL;
       }
-      return hip_status(bmm::launch_mma_tiled(a, s), "mma_tile tiled launch");
-    default: return hip_status(bmm::launch_mma_skinny(a, s), "mma_tile skinny launch");
+      return hip_status(bmm::launch_mma_tiled(a0, s), "mma_tile tiled launch");
+    default: return hip_status(bmm::launch_mma_skinny(a0, s), "mma_tile skinny launch");
   }
+}
+
+}  // namespace
+
+int bmm_mma_tile_with(float* D, const uint32_t* A, const uint32_t* B, const float* C,
+                      float c_scalar, int64_t batch, int64_t M_rep, int64_t N_rep,
+                      int64_t K_rep, bmm_dtype dtype, int32_t kernel, void* stream) {
+  const bmm::MmaArgs a{D, A, B, C, c_scalar, batch, M_rep, N_rep, K_rep, int(dtype), 0, 1.f, 1.f};
+  return mma_common(a, kernel, stream);
+}
+
+int bmm_mma_tile_scaled(float* D, const uint32_t* A, const uint32_t* B, const float* C,
+                        float c_scalar, float alpha, float beta, int64_t batch, int64_t M_rep,
+                        int64_t N_rep, int64_t K_rep, bmm_dtype dtype, int32_t kernel,
+                        void* stream) {
+  const bmm::MmaArgs a{D, A, B, C, c_scalar, batch, M_rep, N_rep, K_rep, int(dtype), 1, alpha, beta};
+  return mma_common(a, kernel, stream);
 }
 
 int bmm_mma_tile(float* D, const uint32_t* A, const uint32_t* B, const float* C,

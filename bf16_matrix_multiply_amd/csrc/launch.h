@@ -16,6 +16,10 @@ struct MmaArgs {
   float c_scalar;
   int64_t batch, M_rep, N_rep, K_rep;
   int dtype;
+  // alpha/beta form: accumulate the product from zero, then
+  // D = fma(alpha, acc, beta * C) (C or c_scalar) in the epilogue.
+  int scaled;
+  float alpha, beta;
 };
 
 hipError_t launch_pack(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,

@@ -42,11 +42,13 @@ __global__ __launch_bounds__(kDirectWaves* kWave) void mma_direct_kernel(MmaArgs
   const bool n_ok = na < p.N_rep;
   const int64_t d_off = ((bm * p.N_rep + na) * 16 + m) * 8 + 4 * (g & 1);
 
-  f32x4 acc;
-  if (p.C) {
-    acc = n_ok ? load16f(p.C + d_off) : f32x4{0.f, 0.f, 0.f, 0.f};
-  } else {
-    acc = f32x4{p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (!p.scaled) {
+    if (p.C) {
+      if (n_ok) acc = load16f(p.C + d_off);
+    } else {
+      acc = f32x4{p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
+    }
   }
 
   // Operand fragments: A row m, B row n = lane % 16 of this tile's 16 columns.
@@ -75,7 +77,14 @@ __global__ __launch_bounds__(kDirectWaves* kWave) void mma_direct_kernel(MmaArgs
     const u32x4 b0 = (b_ok && kr < p.K_rep) ? load16(b_ptr + kr * kAtomWordsB) : zero;
     acc = mfma_16x16x32<DT>(b0, a0, acc);
   }
-  if (n_ok) store16f(p.D + d_off, acc);
+  if (!n_ok) return;
+  if (p.scaled) {
+    // alpha/beta form: C is read here, after the product
+    const f32x4 cv = p.C ? load16f(p.C + d_off) : f32x4{p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(p.alpha, acc[e], p.beta * cv[e]);
+  }
+  store16f(p.D + d_off, acc);
 }
 
 }  // namespace

@@ -29,7 +29,7 @@ constexpr int kUnroll = 4;       // K steps whose loads are issued together
 
 constexpr int kWaves = 8;        // waves per workgroup, one contiguous K chunk each
 
-template <int DT, int MR, bool kHasC>
+template <int DT, int MR, bool kHasC, bool kScaled>
 __global__ __launch_bounds__(kWaves* kWave) void mma_skinny_kernel(MmaArgs p) {
   constexpr int W = kWaves;
   __shared__ __attribute__((aligned(16))) f32x4 red[W][MR][kNBlocks][kWave];
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kWaves* kWave) void mma_skinny_kernel(MmaArgs p) {
 #pragma unroll
     for (int nb = 0; nb < kNBlocks; ++nb) {
       f32x4 v = {0.f, 0.f, 0.f, 0.f};
-      if (wave == 0) {
+      if (!kScaled && wave == 0) {
         if constexpr (kHasC) {
           const int64_t na = d_col0 + 2 * nb;
           if (a_ok[mi] && na < p.N_rep)
@@ -145,8 +145,17 @@ __global__ __launch_bounds__(kWaves* kWave) void mma_skinny_kernel(MmaArgs p) {
     for (int w = 1; w < W; ++w) sum += red[w][mi][nb][l];
     const int lm = l & 15, lg = l >> 4;
     const int64_t ma = m_atom0 + mi, na = nt * kNAtoms + 2 * nb + (lg >> 1);
-    if (ma < p.M_rep && na < p.N_rep)
-      store16f(p.D + (((b * p.M_rep + ma) * p.N_rep + na) * 16 + lm) * 8 + 4 * (lg & 1), sum);
+    if (ma < p.M_rep && na < p.N_rep) {
+      const int64_t off = (((b * p.M_rep + ma) * p.N_rep + na) * 16 + lm) * 8 + 4 * (lg & 1);
+      if constexpr (kScaled) {
+        // alpha/beta form: C is read here, after the product
+        f32x4 cv = {p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
+        if constexpr (kHasC) cv = load16f(p.C + off);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sum[e] = __builtin_fmaf(p.alpha, sum[e], p.beta * cv[e]);
+      }
+      store16f(p.D + off, sum);
+    }
   }
 }
 
@@ -157,10 +166,9 @@ hipError_t launch_mr(const MmaArgs& a, hipStream_t s) {
   if (n_tiles > 0x7fffffff || m_groups > 65535 || a.batch > 65535)
     return hipErrorInvalidConfiguration;
   dim3 grid(unsigned(n_tiles), unsigned(m_groups), unsigned(a.batch));
-  if (a.C)
-    hipLaunchKernelGGL((mma_skinny_kernel<DT, MR, true>), grid, dim3(kWaves * kWave), 0, s, a);
-  else
-    hipLaunchKernelGGL((mma_skinny_kernel<DT, MR, false>), grid, dim3(kWaves * kWave), 0, s, a);
+  auto kern = a.scaled ? (a.C ? mma_skinny_kernel<DT, MR, true, true> : mma_skinny_kernel<DT, MR, false, true>)
+                       : (a.C ? mma_skinny_kernel<DT, MR, true, false> : mma_skinny_kernel<DT, MR, false, false>);
+  hipLaunchKernelGGL(kern, grid, dim3(kWaves * kWave), 0, s, a);
   return hipGetLastError();
 }
 

@@ -46,6 +46,8 @@
 // linear tile index is remapped so each XCD receives a contiguous run of
 // tiles, and runs are rasterised in bands of 8 M tiles, so the tiles that
 // share A rows and B columns run on the same XCD and share its L2.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -122,7 +124,7 @@ __device__ __forceinline__ TileCoord tile_of(int64_t w, int64_t n_tiles, int64_t
   return c;
 }
 
-template <int DT, bool kHasC>
+template <int DT, bool kHasC, bool kScaled>
 __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64_t n_tiles,
                                                                int64_t MT, int64_t NT) {
   // Four separate objects (not one array) so that the compiler can tell the
@@ -193,7 +195,13 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
       (((tc.b * p.M_rep + lane_row_atom) * p.N_rep + lane_col_atom) * 16 + (lane & 15)) * 8 +
       4 * (lane >> 5);
   const int64_t d_mstride = p.N_rep * kAtomFloats;  // next M atom
-  if constexpr (kHasC) {
+  if constexpr (kScaled) {
+    // alpha/beta form: the product starts from zero, C is read in the epilogue
+#pragma unroll
+    for (int pm = 0; pm < kWaveBlocksM; ++pm)
+#pragma unroll
+      for (int qn = 0; qn < kWaveBlocksN; ++qn) acc[pm][qn] = f32x16{};
+  } else if constexpr (kHasC) {
     // Blocks outside a ragged last tile read a clamped (valid) address: their
     // accumulators are never stored, and one branch-free path keeps the 256
     // accumulator registers in place.
@@ -300,10 +308,20 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
     for (int qn = 0; qn < kWaveBlocksN; ++qn)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const f32x4 v = {acc[pm][qn][4 * q + 0], acc[pm][qn][4 * q + 1], acc[pm][qn][4 * q + 2],
-                         acc[pm][qn][4 * q + 3]};
+        f32x4 v = {acc[pm][qn][4 * q + 0], acc[pm][qn][4 * q + 1], acc[pm][qn][4 * q + 2],
+                   acc[pm][qn][4 * q + 3]};
         float* dst = p.D + d_lane + 2 * pm * d_mstride + (4 * qn + q) * kAtomFloats;
-        if (interior || (lane_row_atom + 2 * pm < p.M_rep && lane_col_atom + 4 * qn + q < p.N_rep))
+        const bool ok =
+            interior || (lane_row_atom + 2 * pm < p.M_rep && lane_col_atom + 4 * qn + q < p.N_rep);
+        if constexpr (kScaled) {
+          f32x4 cv = {p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
+          if constexpr (kHasC) {
+            if (ok) cv = load16f(p.C + (dst - p.D));
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.alpha, v[e], p.beta * cv[e]);
+        }
+        if (ok)
           store16f(dst, v);
       }
 }
@@ -317,8 +335,14 @@ hipError_t launch_mma_tiled(const MmaArgs& a, hipStream_t s) {
   if (n_tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
   // Buffer offsets inside one tile's 16 A atom rows must stay below 2^31.
   if (a.K_rep >= kTiledMaxKRep) return hipErrorInvalidValue;
-  auto kern = a.dtype == kBF16 ? (a.C ? mma_tiled_kernel<kBF16, true> : mma_tiled_kernel<kBF16, false>)
-                               : (a.C ? mma_tiled_kernel<kF16, true> : mma_tiled_kernel<kF16, false>);
+  auto pick = [&](auto dt) {
+    constexpr int D = decltype(dt)::value;
+    if (a.scaled)
+      return a.C ? mma_tiled_kernel<D, true, true> : mma_tiled_kernel<D, false, true>;
+    return a.C ? mma_tiled_kernel<D, true, false> : mma_tiled_kernel<D, false, false>;
+  };
+  auto kern = a.dtype == kBF16 ? pick(std::integral_constant<int, kBF16>{})
+                               : pick(std::integral_constant<int, kF16>{});
   hipLaunchKernelGGL(kern, dim3(unsigned(n_tiles)), dim3(kThreads), 0, s, a, n_tiles, MT, NT);
   return hipGetLastError();
 }

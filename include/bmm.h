@@ -176,6 +176,25 @@ int bmm_mma_tile_with(float* D, const uint32_t* A, const uint32_t* B, const floa
                       float c_scalar, int64_t batch, int64_t M_rep, int64_t N_rep,
                       int64_t K_rep, bmm_dtype dtype, int32_t kernel, void* stream);
 
+/*
+ * bmm_mma_tile_scaled — D = alpha * (A * B^T) + beta * C, scaling at the call site.
+ *
+ * The mma.sync page ("Accumulation, transpose and alpha/beta") puts alpha/beta
+ * scaling before or after the MMA at the call site, with the intended
+ * rounding order; this entry point fixes that order: the product is
+ * accumulated from zero (K ascending between 32-deep hardware steps), then
+ *   D = fma(alpha, acc, fl(beta * C))
+ * with one rounding for the final multiply-add (the fma page: a*b+c is one
+ * fused operation). C (or c_scalar when C is NULL) is read once, in the
+ * epilogue; D == C in place is allowed. Operands, layouts, kernel choice and
+ * errors as bmm_mma_tile_with. alpha = beta = 1 differs from bmm_mma_tile
+ * only in where C enters the sum (it is added last here, first there).
+ */
+int bmm_mma_tile_scaled(float* D, const uint32_t* A, const uint32_t* B, const float* C,
+                        float c_scalar, float alpha, float beta, int64_t batch, int64_t M_rep,
+                        int64_t N_rep, int64_t K_rep, bmm_dtype dtype, int32_t kernel,
+                        void* stream);
+
 /* Which kernel AUTO would run for this shape (a bmm_kernel value), or < 0. */
 int bmm_select_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep);
 

@@ -55,6 +55,8 @@ class Oracle:
         L.oracle_mma.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64, i64, ctypes.c_int]
         L.oracle_mma_sampled.argtypes = [p, p, i64, p, p, p, ctypes.c_float, i64, i64, i64,
                                          i64, ctypes.c_int]
+        L.oracle_mma_scaled.argtypes = [p, p, p, p, ctypes.c_float, ctypes.c_float,
+                                        ctypes.c_float, i64, i64, i64, i64, ctypes.c_int]
         L.oracle_box_copy.restype = i64
         L.oracle_box_copy.argtypes = [p, p, i32, i32, p, p, p, p, i32, p]
         self.L = L
@@ -119,6 +121,19 @@ class Oracle:
                                N_rep, K_rep, _DTYPES[dtype])
         if rc != 0:
             raise ValueError("oracle_mma rejected its arguments")
+        return D
+
+    def mma_scaled(self, A, B, C, c, alpha, beta, dtype) -> np.ndarray:
+        """D = fma(alpha, A * B^T (from zero), fl(beta * C)), full output."""
+        A = np.ascontiguousarray(A, np.uint32)
+        B = np.ascontiguousarray(B, np.uint32)
+        C = None if C is None else np.ascontiguousarray(C, np.float32)
+        batch, M_rep, N_rep, K_rep = _mma_shapes(A, B, C)
+        D = np.empty((batch, M_rep, N_rep, 16, 8), np.float32)
+        rc = self.L.oracle_mma_scaled(_ptr(D), _ptr(A), _ptr(B), _ptr(C), float(c), float(alpha),
+                                      float(beta), batch, M_rep, N_rep, K_rep, _DTYPES[dtype])
+        if rc != 0:
+            raise ValueError("oracle_mma_scaled rejected its arguments")
         return D
 
     def mma_sampled(self, A, B, C, c, dtype, idx: np.ndarray) -> np.ndarray:
@@ -230,6 +245,10 @@ def mma(A, B, C, c, dtype):
 
 def mma_sampled(A, B, C, c, dtype, idx):
     return default().mma_sampled(A, B, C, c, dtype, idx)
+
+
+def mma_scaled(A, B, C, c, alpha, beta, dtype):
+    return default().mma_scaled(A, B, C, c, alpha, beta, dtype)
 
 
 def bound(A, B, C, c, dtype, idx=None):

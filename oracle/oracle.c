@@ -186,6 +186,39 @@ int oracle_mma(float* D, const uint32_t* A, const uint32_t* B, const float* C, f
   return 0;
 }
 
+/* alpha/beta form, with the scaling at the call site (mma.sync page,
+ * "Accumulation, transpose and alpha/beta"): the product is accumulated from
+ * zero, k ascending, then D = fma(alpha, acc, fl(beta * C)) -- one rounding
+ * for the final multiply-add (fma page, "Operand specification"). */
+static float one_output_scaled(const uint32_t* A, const uint32_t* B, const float* C, float c,
+                               float alpha, float beta, int64_t b, int64_t m, int64_t n,
+                               int64_t M_rep, int64_t N_rep, int64_t K_rep, int dtype) {
+  float acc = 0.0f;
+  for (int64_t k = 0; k < 16 * K_rep; ++k) {
+    float a = packed_elem(A, b, m, k, 16, M_rep, K_rep, dtype);
+    float x = packed_elem(B, b, n, k, 8, N_rep, K_rep, dtype);
+    acc = acc + a * x;
+  }
+  const float cv = C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c;
+  const float t = beta * cv;
+  return fmaf(alpha, acc, t);
+}
+
+int oracle_mma_scaled(float* D, const uint32_t* A, const uint32_t* B, const float* C, float c,
+                      float alpha, float beta, int64_t batch, int64_t M_rep, int64_t N_rep,
+                      int64_t K_rep, int dtype) {
+  if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+  const int64_t rows = batch * 16 * M_rep;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t bm = 0; bm < rows; ++bm) {
+    const int64_t b = bm / (16 * M_rep), m = bm % (16 * M_rep);
+    for (int64_t n = 0; n < 8 * N_rep; ++n)
+      D[acc_offset(b, m, n, M_rep, N_rep)] =
+          one_output_scaled(A, B, C, c, alpha, beta, b, m, n, M_rep, N_rep, K_rep, dtype);
+  }
+  return 0;
+}
+
 /* Selected outputs only: idx holds count triples (b, m, n); out[i] gets D[b, m, n]. */
 int oracle_mma_sampled(float* out, const int64_t* idx, int64_t count, const uint32_t* A,
                        const uint32_t* B, const float* C, float c, int64_t batch,

@@ -132,6 +132,66 @@ def pin_quarter_closed_form(o):
         assert np.array_equal((D2 * 16).astype(np.int64), prod - 20), (dt, "scalar")
 
 
+def pin_scaled(o):
+    """alpha/beta form: with quarter-integer data and power-of-two alpha, beta
+    every step is exact, so 16*D = alpha*sum_k(4a)(4b) + beta*16*C in int64;
+    alpha=1, beta=1 on the same data equals the plain recurrence; on normal
+    data the result is within gamma_K of the float64 value of
+    alpha*A*B^T + beta*C, and differs from C-first accumulation somewhere
+    (the scaling really happens after the sum)."""
+    rng = np.random.default_rng(9)
+    dt, batch, Mr, Nr, Kr = "bf16", 2, 2, 3, 5
+    M, N, K = 16 * Mr, 8 * Nr, 16 * Kr
+    a = _quarter_bits(rng, (batch, M, K), dt)
+    b = _quarter_bits(rng, (batch, N, K), dt)
+    c_int = rng.integers(-64, 65, (batch, M, N))
+    C = util.logical_to_tile((c_int / 4).astype(np.float32))
+    A, B = o.pack(a, 16), o.pack(b, 8)
+    ai = np.rint(4 * util.decode(a, dt)).astype(np.int64)
+    bi = np.rint(4 * util.decode(b, dt)).astype(np.int64)
+    prod = np.einsum("bmk,bnk->bmn", ai, bi)
+    for alpha, beta in ((0.5, -2.0), (4.0, 0.25), (-1.0, 0.0)):
+        D = util.tile_to_logical(o.mma_scaled(A, B, C, 0.0, alpha, beta, dt)).astype(np.float64)
+        assert np.array_equal(D * 16, alpha * prod + beta * 4 * c_int), (alpha, beta)
+    assert np.array_equal(o.mma_scaled(A, B, C, 0.0, 1.0, 1.0, dt), o.mma(A, B, C, 0.0, dt))
+    D = util.tile_to_logical(o.mma_scaled(A, B, None, 1.5, 2.0, -1.0, dt)).astype(np.float64)
+    assert np.array_equal(D * 16, 2.0 * prod - 1.5 * 16)
+    # normal data
+    a = workloads.draw_operand(rng, "normal", (1, 32, 16 * 21), dt)
+    b = workloads.draw_operand(rng, "normal", (1, 24, 16 * 21), dt)
+    Cn = rng.standard_normal((1, 2, 3, 16, 8), dtype=np.float32)
+    A, B = o.pack(a, 16), o.pack(b, 8)
+    alpha, beta = np.float32(0.7), np.float32(-1.3)
+    D = util.tile_to_logical(o.mma_scaled(A, B, Cn, 0.0, alpha, beta, dt)).astype(np.float64)
+    af, bf = util.decode(a, dt), util.decode(b, dt)
+    Cl = util.tile_to_logical(Cn).astype(np.float64)
+    ref = float(alpha) * (af @ bf.transpose(0, 2, 1)) + float(beta) * Cl
+    mag = abs(float(alpha)) * (np.abs(af) @ np.abs(bf).transpose(0, 2, 1)) + abs(float(beta)) * np.abs(Cl)
+    assert (np.abs(D - ref) <= util.gamma(16 * 21 + 3) * mag).all()
+    first = util.tile_to_logical(o.mma(A, B, Cn, 0.0, dt))
+    assert not np.array_equal(util.tile_to_logical(o.mma_scaled(A, B, Cn, 0.0, 1.0, 1.0, dt)), first)
+    # one rounding for the final multiply-add (the fma page's test: the exact
+    # alpha*acc + t lies between representable results)
+    A, B, C, alpha = scaled_rounding_case(dt)
+    D = util.tile_to_logical(o.mma_scaled(A, B, C, 0.0, alpha, 1.0, dt))
+    assert D[0, 0, 0] == np.float32(2.0 ** -46), D[0, 0, 0]
+
+
+def scaled_rounding_case(dt):
+    """acc[0,0] = 1 + 2^-23 (from 1*1 + 2^-12 * 2^-11), alpha = 1 + 2^-23,
+    beta*C = -(1 + 2^-22): fma gives 2^-46, a rounded multiply then add 0."""
+    a = np.zeros((1, 16, 16), np.float32)
+    b = np.zeros((1, 8, 16), np.float32)
+    a[0, 0, 0], a[0, 0, 1] = 1.0, 2.0 ** -12
+    b[0, 0, 0], b[0, 0, 1] = 1.0, 2.0 ** -11
+    to_bits = workloads.f32_to_bf16_bits if dt == "bf16" else workloads.f32_to_f16_bits
+    A = util.page_recipe_pack(to_bits(a), 16)
+    B = util.page_recipe_pack(to_bits(b), 8)
+    C = np.zeros((1, 1, 1, 16, 8), np.float32)
+    C[0, 0, 0, 0, 0] = -(1.0 + 2.0 ** -22)
+    return A, B, C, np.float32(1.0 + 2.0 ** -23)
+
+
 def pin_normal_vs_float64(o):
     """Normal inputs: |D - D_f64| <= gamma_K * (|A||B|^T + |C|) elementwise,
     the worst-case bound of K sequential fp32 additions, against float64 numpy

@@ -202,3 +202,86 @@ def test_full_quantised_variants(name):
     inp = workloads.make_inputs(w, seed=1)
     _, _, _, D = gu.gpu_run(w, inp)
     gu.assert_parity_sampled(w, inp, D)
+
+
+# ---- alpha/beta form (bmm_mma_tile_scaled) ----
+
+SCALED = {
+    "q_272x264x336_ct": C(1, 272, 264, 336, "bf16", "quarter", "quarter", c_tensor=True),
+    "q_f16_b2_48x40x80_scalar": C(2, 48, 40, 80, "f16", "quarter", "quarter", c_scalar=1.25),
+    "q_16x1032x1040_ct": C(1, 16, 1032, 1040, "bf16", "quarter", "quarter", c_tensor=True),
+    "n_512x520x528_ct": C(1, 512, 520, 528, "bf16", c_tensor=True),
+}
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+@pytest.mark.parametrize("case", sorted(SCALED))
+def test_scaled_parity(case, kernel):
+    """Quarter-integer data with power-of-two alpha, beta: bit-exact against
+    the oracle's alpha/beta form; normal data within
+    1e-3 (|alpha||A||B|^T + |beta||C|)."""
+    w = SCALED[case]
+    inp = inputs(w)
+    A = bmm.pack_operand(gu.dev_u16(inp["a"]), 16)
+    B = bmm.pack_operand(gu.dev_u16(inp["b"]), 8)
+    Cd = None if inp["c_tensor"] is None else torch.from_numpy(inp["c_tensor"]).cuda()
+    alpha, beta = (0.5, -2.0) if w.exact else (0.7, -1.3)
+    out = torch.full((w.batch, w.M_rep, w.N_rep, 16, 8), float("nan"), device="cuda")
+    D = bmm.mma_tile(A, B, Cd, float(inp["c_scalar"]), w.dtype, out=out, kernel=kernel,
+                     alpha=alpha, beta=beta).cpu().numpy()
+    Ao, Bo = gu.oracle_operands(w, inp)
+    ref = oracle.mma_scaled(Ao, Bo, inp["c_tensor"], inp["c_scalar"], alpha, beta, w.dtype)
+    assert not np.isnan(D).any()
+    if w.exact:
+        assert np.array_equal(D, ref)
+    else:
+        prod = oracle.bound(Ao, Bo, None, 0.0, w.dtype)          # |A||B|^T
+        cmag = np.abs(inp["c_tensor"]) if inp["c_tensor"] is not None else abs(inp["c_scalar"])
+        bnd = abs(alpha) * prod.astype(np.float64) + abs(beta) * cmag
+        assert (np.abs(D.astype(np.float64) - ref) <= 1e-3 * bnd).all()
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_scaled_single_rounding(kernel):
+    """The final alpha*acc + beta*C is one fused operation: for acc = 1+2^-23,
+    alpha = 1+2^-23, beta*C = -(1+2^-22) the result is 2^-46 (a rounded
+    multiply followed by an add would give 0)."""
+    from tests import pins
+    A, B, Cn, alpha = pins.scaled_rounding_case("bf16")
+    Ad = torch.from_numpy(A.view(np.int32)).cuda()
+    Bd = torch.from_numpy(B.view(np.int32)).cuda()
+    Cd = torch.from_numpy(Cn).cuda()
+    D = bmm.mma_tile(Ad, Bd, Cd, 0.0, "bf16", kernel=kernel, alpha=float(alpha), beta=1.0)
+    assert D.cpu().numpy()[0, 0, 0, 0, 0] == np.float32(2.0 ** -46)
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
+def test_scaled_in_place(kernel):
+    w = C(1, 272, 136, 144, "f16", "quarter", "quarter", c_tensor=True)
+    inp = inputs(w)
+    A = bmm.pack_operand(gu.dev_u16(inp["a"]), 16)
+    B = bmm.pack_operand(gu.dev_u16(inp["b"]), 8)
+    Cd = torch.from_numpy(inp["c_tensor"]).cuda()
+    ref = bmm.mma_tile(A, B, Cd, 0.0, "f16", kernel=kernel, alpha=0.25, beta=4.0).cpu().numpy()
+    bmm.mma_tile(A, B, Cd, 0.0, "f16", out=Cd, kernel=kernel, alpha=0.25, beta=4.0)
+    assert np.array_equal(Cd.cpu().numpy(), ref)
+
+
+def test_scaled_full_8192():
+    """8192^3 bf16, C tensor, alpha=0.7, beta=-1.3: sampled outputs within
+    1e-3 (|alpha||A||B|^T + |beta||C|) of alpha*P + beta*C, P the oracle's
+    product accumulated from zero."""
+    w = workloads.WORKLOADS["gemm_8192_bf16_ctensor"]
+    inp = inputs(w)
+    A = bmm.pack_operand(gu.dev_u16(inp["a"]), 16)
+    B = bmm.pack_operand(gu.dev_u16(inp["b"]), 8)
+    Cd = torch.from_numpy(inp["c_tensor"]).cuda()
+    D = util.tile_to_logical(bmm.mma_tile(A, B, Cd, 0.0, "bf16", alpha=0.7, beta=-1.3).cpu().numpy())
+    Ao, Bo = gu.oracle_operands(w, inp)
+    idx = util.sample_indices(np.random.default_rng(5), 1, w.M, w.N, 1024)
+    P = oracle.mma_sampled(Ao, Bo, None, 0.0, "bf16", idx).astype(np.float64)
+    Cl = util.tile_to_logical(inp["c_tensor"])[idx[:, 0], idx[:, 1], idx[:, 2]].astype(np.float64)
+    ref = np.float32(0.7) * P + np.float32(-1.3) * Cl
+    mag = 0.7 * oracle.bound(Ao, Bo, None, 0.0, "bf16", idx) + 1.3 * np.abs(Cl)
+    got = D[idx[:, 0], idx[:, 1], idx[:, 2]].astype(np.float64)
+    assert (np.abs(got - ref) <= 1e-3 * mag).all()

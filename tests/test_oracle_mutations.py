@@ -27,9 +27,9 @@ MUTATIONS = {
         "* R + (R - 1 - row % R)) * 8 + (k % 16) / 2];\n  return oracle_h2f",
         ["pin_page_example", "pin_quarter_closed_form", "pin_normal_vs_float64"]),
     "c_added_at_every_k16_issue": (
-        "acc = acc + a * x;",
+        "acc = acc + a * x;\n  }\n  return acc;",
         "acc = acc + a * x;\n    if (k % 16 == 15 && k + 1 < 16 * K_rep)"
-        " acc = acc + (C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c);",
+        " acc = acc + (C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c);\n  }\n  return acc;",
         ["pin_quarter_closed_form", "pin_recurrence_chain", "pin_zero_a_and_scalar"]),
     "c_ignored": (
         "float acc = C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c;", "float acc = 0.0f;",
@@ -42,12 +42,17 @@ MUTATIONS = {
         "* N_rep + n / 8) * 8 + n % 8) * 16 + m % 16;",
         ["pin_page_example", "pin_quarter_closed_form"]),
     "last_k_atom_dropped": (
-        "k < 16 * K_rep; ++k) {\n    float a", "k < 16 * K_rep - 16; ++k) {\n    float a",
+        ": c;\n  for (int64_t k = 0; k < 16 * K_rep; ++k) {",
+        ": c;\n  for (int64_t k = 0; k < 16 * K_rep - 16; ++k) {",
         ["pin_page_example", "pin_quarter_closed_form"]),
     "kmajor_k_and_row_strides_swapped": (
         "uint32_t lo = col[(16 * kr + 2 * w) * ld];\n            uint32_t hi = col[(16 * kr + 2 * w + 1) * ld];",
         "uint32_t lo = col[(16 * kr + 2 * w) * ld];\n            uint32_t hi = col[(16 * kr + 2 * w) * ld + 1];",
         ["pin_pack_kmajor"]),
+    "scaled_two_roundings": (
+        "return fmaf(alpha, acc, t);", "return alpha * acc + t;", ["pin_scaled"]),
+    "scaled_beta_ignored": (
+        "const float t = beta * cv;", "const float t = cv;", ["pin_scaled"]),
     "box_fill_not_zero": (
         "memset(out, 0, (size_t)elem_bytes);", "memset(out, 0x5a, (size_t)elem_bytes);",
         ["pin_box_oob"]),
