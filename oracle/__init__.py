@@ -52,6 +52,11 @@ class Oracle:
         L.oracle_pack.argtypes = [p, p, i64, i64, i64, i64, i64]
         L.oracle_unpack.argtypes = [p, p, i64, i64, i64, i64]
         L.oracle_pack_kmajor.argtypes = [p, p, i64, i64, i64, i64, i64]
+        L.oracle_pack_k8.argtypes = [p, p, i64, i64, i64, i64, i64]
+        L.oracle_mma_k.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64, i64, i64,
+                                   ctypes.c_int]
+        L.oracle_mma_sampled_k.argtypes = [p, p, i64, p, p, p, ctypes.c_float, i64, i64, i64,
+                                           i64, i64, ctypes.c_int]
         L.oracle_mma.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64, i64, ctypes.c_int]
         L.oracle_mma_sampled.argtypes = [p, p, i64, p, p, p, ctypes.c_float, i64, i64, i64,
                                          i64, ctypes.c_int]
@@ -98,6 +103,49 @@ class Oracle:
         rc = self.L.oracle_pack_kmajor(_ptr(out), _ptr(x), batch, rows, K, ld, atom_rows)
         if rc != 0:
             raise ValueError("oracle_pack_kmajor rejected its arguments")
+        return out
+
+    def pack_k8(self, x: np.ndarray, atom_rows: int) -> np.ndarray:
+        """(batch, rows, K) uint16 -> (batch, rows/R, K/8, R, 4) uint32 words
+        (atom K = 8, the m16n8k8 layout)."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        if x.ndim == 2:
+            x = x[None]
+        batch, rows, K = x.shape
+        out = np.empty((batch, rows // atom_rows, K // 8, atom_rows, 4), np.uint32)
+        if self.L.oracle_pack_k8(_ptr(out), _ptr(x), batch, rows, K, K, atom_rows) != 0:
+            raise ValueError("oracle_pack_k8 rejected its arguments")
+        return out
+
+    def mma_k8(self, A, B, C, c, dtype) -> np.ndarray:
+        """D = A * B^T + C over k=8-atom operands (batch, M/16, K/8, 16, 4) and
+        (batch, N/8, K/8, 8, 4)."""
+        A = np.ascontiguousarray(A, np.uint32)
+        B = np.ascontiguousarray(B, np.uint32)
+        C = None if C is None else np.ascontiguousarray(C, np.float32)
+        batch, M_rep, K_rep, ra, wa = A.shape
+        b2, N_rep, K2, rb, wb = B.shape
+        assert (ra, wa, rb, wb) == (16, 4, 8, 4) and b2 == batch and K2 == K_rep
+        D = np.empty((batch, M_rep, N_rep, 16, 8), np.float32)
+        rc = self.L.oracle_mma_k(_ptr(D), _ptr(A), _ptr(B), _ptr(C), float(c), batch, M_rep,
+                                 N_rep, K_rep, 8, _DTYPES[dtype])
+        if rc != 0:
+            raise ValueError("oracle_mma_k rejected its arguments")
+        return D
+
+    def mma_k8_sampled(self, A, B, C, c, dtype, idx) -> np.ndarray:
+        A = np.ascontiguousarray(A, np.uint32)
+        B = np.ascontiguousarray(B, np.uint32)
+        C = None if C is None else np.ascontiguousarray(C, np.float32)
+        batch, M_rep, K_rep = A.shape[:3]
+        N_rep = B.shape[1]
+        idx = np.ascontiguousarray(idx, np.int64).reshape(-1, 3)
+        out = np.empty(len(idx), np.float32)
+        rc = self.L.oracle_mma_sampled_k(_ptr(out), _ptr(idx), len(idx), _ptr(A), _ptr(B),
+                                         _ptr(C), float(c), batch, M_rep, N_rep, K_rep, 8,
+                                         _DTYPES[dtype])
+        if rc != 0:
+            raise ValueError("oracle_mma_sampled_k rejected its arguments")
         return out
 
     def unpack(self, p: np.ndarray, atom_rows: int) -> np.ndarray:
@@ -237,6 +285,18 @@ def unpack(p, atom_rows):
 
 def pack_kmajor(x, atom_rows, rows=None):
     return default().pack_kmajor(x, atom_rows, rows)
+
+
+def pack_k8(x, atom_rows):
+    return default().pack_k8(x, atom_rows)
+
+
+def mma_k8(A, B, C, c, dtype):
+    return default().mma_k8(A, B, C, c, dtype)
+
+
+def mma_k8_sampled(A, B, C, c, dtype, idx):
+    return default().mma_k8_sampled(A, B, C, c, dtype, idx)
 
 
 def mma(A, B, C, c, dtype):

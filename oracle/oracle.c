@@ -128,6 +128,28 @@ int oracle_pack_kmajor(uint32_t* P, const uint16_t* X, int64_t batch, int64_t ro
   return 0;
 }
 
+/* Packing with an atom K of 8 (the m16n8k8 form of the mma.sync page's
+ * introduction; shapes table with k = 8): A is (rows/16, K/8, 16, 4) words,
+ * B (rows/8, K/8, 8, 4):
+ *   P[b, r, kr, i, w] = X[b, R*r+i, 8*kr+2*w] | X[b, R*r+i, 8*kr+2*w+1] << 16, w < 4
+ */
+int oracle_pack_k8(uint32_t* P, const uint16_t* X, int64_t batch, int64_t rows, int64_t K,
+                   int64_t ld, int64_t R) {
+  if ((R != 16 && R != 8) || rows % R || K % 8 || ld < K) return -1;
+  const int64_t rows_rep = rows / R, K_rep = K / 8;
+  for (int64_t b = 0; b < batch; ++b)
+    for (int64_t r = 0; r < rows_rep; ++r)
+      for (int64_t kr = 0; kr < K_rep; ++kr)
+        for (int64_t i = 0; i < R; ++i)
+          for (int64_t w = 0; w < 4; ++w) {
+            const uint16_t* src_row = X + b * rows * ld + (R * r + i) * ld;
+            uint32_t lo = src_row[8 * kr + 2 * w];
+            uint32_t hi = src_row[8 * kr + 2 * w + 1];
+            P[(((b * rows_rep + r) * K_rep + kr) * R + i) * 4 + w] = lo | (hi << 16);
+          }
+  return 0;
+}
+
 /* Inverse of oracle_pack into a dense (batch, rows, K) array. */
 int oracle_unpack(uint16_t* X, const uint32_t* P, int64_t batch, int64_t rows, int64_t K,
                   int64_t R) {
@@ -145,11 +167,13 @@ int oracle_unpack(uint16_t* X, const uint32_t* P, int64_t batch, int64_t rows, i
 
 /* ---- multiply-accumulate ---- */
 
-/* Logical element (row, k) of a packed operand with atom height R. */
+/* Logical element (row, k) of a packed operand with atom height R and atom
+ * K ka (16, or 8 for the m16n8k8 form): atom (row/R, k/ka), atom row row%R,
+ * word (k%ka)/2, half k%2. */
 static float packed_elem(const uint32_t* P, int64_t b, int64_t row, int64_t k, int64_t R,
-                         int64_t rows_rep, int64_t K_rep, int dtype) {
+                         int64_t rows_rep, int64_t K_rep, int64_t ka, int dtype) {
   uint32_t word =
-      P[(((b * rows_rep + row / R) * K_rep + k / 16) * R + row % R) * 8 + (k % 16) / 2];
+      P[(((b * rows_rep + row / R) * K_rep + k / ka) * R + row % R) * (ka / 2) + (k % ka) / 2];
   return oracle_h2f((uint16_t)((word >> (16 * (k % 2))) & 0xFFFFu), dtype);
 }
 
@@ -161,29 +185,37 @@ static int64_t acc_offset(int64_t b, int64_t m, int64_t n, int64_t M_rep, int64_
 /* One output element: acc starts at C (read once), then every k in order. */
 static float one_output(const uint32_t* A, const uint32_t* B, const float* C, float c,
                         int64_t b, int64_t m, int64_t n, int64_t M_rep, int64_t N_rep,
-                        int64_t K_rep, int dtype) {
+                        int64_t K_rep, int64_t ka, int dtype) {
   float acc = C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c;
-  for (int64_t k = 0; k < 16 * K_rep; ++k) {
-    float a = packed_elem(A, b, m, k, 16, M_rep, K_rep, dtype);
-    float x = packed_elem(B, b, n, k, 8, N_rep, K_rep, dtype);
+  for (int64_t k = 0; k < ka * K_rep; ++k) {
+    float a = packed_elem(A, b, m, k, 16, M_rep, K_rep, ka, dtype);
+    float x = packed_elem(B, b, n, k, 8, N_rep, K_rep, ka, dtype);
     acc = acc + a * x;
   }
   return acc;
 }
 
-/* D = A * B^T + C over the whole problem. C == NULL selects the scalar c. */
-int oracle_mma(float* D, const uint32_t* A, const uint32_t* B, const float* C, float c,
-               int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep, int dtype) {
+/* D = A * B^T + C over the whole problem. C == NULL selects the scalar c;
+ * ka is the atom K (16, or 8 for the m16n8k8 layout). */
+int oracle_mma_k(float* D, const uint32_t* A, const uint32_t* B, const float* C, float c,
+                 int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep, int64_t ka,
+                 int dtype) {
   if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+  if (ka != 16 && ka != 8) return -1;
   const int64_t rows = batch * 16 * M_rep;
 #pragma omp parallel for schedule(dynamic)
   for (int64_t bm = 0; bm < rows; ++bm) {
     const int64_t b = bm / (16 * M_rep), m = bm % (16 * M_rep);
     for (int64_t n = 0; n < 8 * N_rep; ++n)
       D[acc_offset(b, m, n, M_rep, N_rep)] =
-          one_output(A, B, C, c, b, m, n, M_rep, N_rep, K_rep, dtype);
+          one_output(A, B, C, c, b, m, n, M_rep, N_rep, K_rep, ka, dtype);
   }
   return 0;
+}
+
+int oracle_mma(float* D, const uint32_t* A, const uint32_t* B, const float* C, float c,
+               int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep, int dtype) {
+  return oracle_mma_k(D, A, B, C, c, batch, M_rep, N_rep, K_rep, 16, dtype);
 }
 
 /* alpha/beta form, with the scaling at the call site (mma.sync page,
@@ -195,8 +227,8 @@ static float one_output_scaled(const uint32_t* A, const uint32_t* B, const float
                                int64_t M_rep, int64_t N_rep, int64_t K_rep, int dtype) {
   float acc = 0.0f;
   for (int64_t k = 0; k < 16 * K_rep; ++k) {
-    float a = packed_elem(A, b, m, k, 16, M_rep, K_rep, dtype);
-    float x = packed_elem(B, b, n, k, 8, N_rep, K_rep, dtype);
+    float a = packed_elem(A, b, m, k, 16, M_rep, K_rep, 16, dtype);
+    float x = packed_elem(B, b, n, k, 8, N_rep, K_rep, 16, dtype);
     acc = acc + a * x;
   }
   const float cv = C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c;
@@ -220,10 +252,11 @@ int oracle_mma_scaled(float* D, const uint32_t* A, const uint32_t* B, const floa
 }
 
 /* Selected outputs only: idx holds count triples (b, m, n); out[i] gets D[b, m, n]. */
-int oracle_mma_sampled(float* out, const int64_t* idx, int64_t count, const uint32_t* A,
-                       const uint32_t* B, const float* C, float c, int64_t batch,
-                       int64_t M_rep, int64_t N_rep, int64_t K_rep, int dtype) {
+int oracle_mma_sampled_k(float* out, const int64_t* idx, int64_t count, const uint32_t* A,
+                         const uint32_t* B, const float* C, float c, int64_t batch,
+                         int64_t M_rep, int64_t N_rep, int64_t K_rep, int64_t ka, int dtype) {
   if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+  if (ka != 16 && ka != 8) return -1;
   for (int64_t i = 0; i < count; ++i) {
     const int64_t *t = idx + 3 * i;
     if (t[0] < 0 || t[0] >= batch || t[1] < 0 || t[1] >= 16 * M_rep || t[2] < 0 ||
@@ -233,8 +266,14 @@ int oracle_mma_sampled(float* out, const int64_t* idx, int64_t count, const uint
 #pragma omp parallel for schedule(dynamic)
   for (int64_t i = 0; i < count; ++i)
     out[i] = one_output(A, B, C, c, idx[3 * i], idx[3 * i + 1], idx[3 * i + 2], M_rep, N_rep,
-                        K_rep, dtype);
+                        K_rep, ka, dtype);
   return 0;
+}
+
+int oracle_mma_sampled(float* out, const int64_t* idx, int64_t count, const uint32_t* A,
+                       const uint32_t* B, const float* C, float c, int64_t batch,
+                       int64_t M_rep, int64_t N_rep, int64_t K_rep, int dtype) {
+  return oracle_mma_sampled_k(out, idx, count, A, B, C, c, batch, M_rep, N_rep, K_rep, 16, dtype);
 }
 
 /* ---- box copy (global tensor region -> compact image) ----

@@ -78,6 +78,32 @@ def pin_pack_kmajor(o):
     assert np.array_equal(P[0], lo | (hi << 16))
 
 
+def pin_k8_layout(o):
+    """Atom K = 8 (m16n8k8 form): the packer equals the page's recipe with
+    8-wide atoms; the multiply-accumulate over k=8-packed operands equals the
+    one over k=16-packed operands of the same matrices bit for bit (same
+    ascending-k recurrence), on normal data with a C tensor, odd K atom
+    counts and batch 2; and matches the int64 closed form on quarter data."""
+    rng = np.random.default_rng(10)
+    for R, rows, K in ((16, 48, 40), (8, 24, 72)):
+        x = util.random_bits(rng, (2, rows, K))
+        assert np.array_equal(o.pack_k8(x, R), util.page_recipe_pack_k8(x, R)), (R, rows, K)
+    dt, batch, Mr, Nr, K = "bf16", 2, 2, 3, 16 * 7
+    a = workloads.draw_operand(rng, "normal", (batch, 16 * Mr, K), dt)
+    b = workloads.draw_operand(rng, "normal", (batch, 8 * Nr, K), dt)
+    C = rng.standard_normal((batch, Mr, Nr, 16, 8), dtype=np.float32)
+    D16 = o.mma(o.pack(a, 16), o.pack(b, 8), C, 0.0, dt)
+    D8 = o.mma_k8(o.pack_k8(a, 16), o.pack_k8(b, 8), C, 0.0, dt)
+    assert np.array_equal(D16, D8)
+    K = 8 * 9   # an odd number of k=8 atoms
+    a = _quarter_bits(rng, (1, 32, K), dt)
+    b = _quarter_bits(rng, (1, 16, K), dt)
+    ai = np.rint(4 * util.decode(a, dt)).astype(np.int64)
+    bi = np.rint(4 * util.decode(b, dt)).astype(np.int64)
+    D = util.tile_to_logical(o.mma_k8(o.pack_k8(a, 16), o.pack_k8(b, 8), None, 0.0, dt))
+    assert np.array_equal((D * 16).astype(np.int64), np.einsum("bmk,bnk->bmn", ai, bi))
+
+
 def pin_roundtrip(o):
     """unpack(pack(x)) == x on all 65536 bit patterns (NaN encodings included),
     for both atom heights: the packer moves bits, never values."""

@@ -23,8 +23,8 @@ MUTATIONS = {
     "f16_subnormal_scale_wrong": (
         "ldexpf((float)frac, -24)", "ldexpf((float)frac, -25)", ["pin_h2f"]),
     "operand_rows_reversed_in_atom": (
-        "* R + row % R) * 8 + (k % 16) / 2];\n  return oracle_h2f",
-        "* R + (R - 1 - row % R)) * 8 + (k % 16) / 2];\n  return oracle_h2f",
+        "* R + row % R) * (ka / 2) + (k % ka) / 2];\n  return oracle_h2f",
+        "* R + (R - 1 - row % R)) * (ka / 2) + (k % ka) / 2];\n  return oracle_h2f",
         ["pin_page_example", "pin_quarter_closed_form", "pin_normal_vs_float64"]),
     "c_added_at_every_k16_issue": (
         "acc = acc + a * x;\n  }\n  return acc;",
@@ -42,8 +42,8 @@ MUTATIONS = {
         "* N_rep + n / 8) * 8 + n % 8) * 16 + m % 16;",
         ["pin_page_example", "pin_quarter_closed_form"]),
     "last_k_atom_dropped": (
-        ": c;\n  for (int64_t k = 0; k < 16 * K_rep; ++k) {",
-        ": c;\n  for (int64_t k = 0; k < 16 * K_rep - 16; ++k) {",
+        ": c;\n  for (int64_t k = 0; k < ka * K_rep; ++k) {",
+        ": c;\n  for (int64_t k = 0; k < ka * K_rep - ka; ++k) {",
         ["pin_page_example", "pin_quarter_closed_form"]),
     "kmajor_k_and_row_strides_swapped": (
         "uint32_t lo = col[(16 * kr + 2 * w) * ld];\n            uint32_t hi = col[(16 * kr + 2 * w + 1) * ld];",
@@ -53,6 +53,13 @@ MUTATIONS = {
         "return fmaf(alpha, acc, t);", "return alpha * acc + t;", ["pin_scaled"]),
     "scaled_beta_ignored": (
         "const float t = beta * cv;", "const float t = cv;", ["pin_scaled"]),
+    "k8_word_stride_as_k16": (
+        "* R + row % R) * (ka / 2) + (k % ka) / 2];", "* R + row % R) * 8 + (k % ka) / 2];",
+        ["pin_k8_layout"]),
+    "k8_pack_halves_swapped": (
+        "P[(((b * rows_rep + r) * K_rep + kr) * R + i) * 4 + w] = lo | (hi << 16);",
+        "P[(((b * rows_rep + r) * K_rep + kr) * R + i) * 4 + w] = hi | (lo << 16);",
+        ["pin_k8_layout"]),
     "box_fill_not_zero": (
         "memset(out, 0, (size_t)elem_bytes);", "memset(out, 0x5a, (size_t)elem_bytes);",
         ["pin_box_oob"]),

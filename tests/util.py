@@ -55,6 +55,14 @@ def page_recipe_pack(x, R):
     return y.view(np.uint32).reshape(b, rows // R, K // 16, R, 8)
 
 
+def page_recipe_pack_k8(x, R):
+    """The same recipe with an atom K of 8 (the m16n8k8 form): (batch, rows, K)
+    uint16 -> (batch, rows/R, K/8, R, 4) uint32."""
+    b, rows, K = x.shape
+    y = np.ascontiguousarray(x.reshape(b, rows // R, R, K // 8, 8).transpose(0, 1, 3, 2, 4))
+    return y.view(np.uint32).reshape(b, rows // R, K // 8, R, 4)
+
+
 def random_bits(rng, shape):
     return rng.integers(0, 1 << 16, shape, dtype=np.uint32).astype(np.uint16)
 
