@@ -115,7 +115,12 @@ def main():
     ap.add_argument("--kmajor", action="store_true",
                     help="A and B are stored K-major (transposed) in HBM; the step packs them "
                          "with pack_operand_kmajor")
+    ap.add_argument("--atom-k", type=int, default=16, choices=[16, 8],
+                    help="K depth of a packed atom: 16, or 8 for the m16n8k8 layout "
+                         "(pack_operand_k8 + mma_tile_opts)")
     args = ap.parse_args()
+    if args.kmajor and args.atom_k != 16:
+        ap.error("--kmajor packs the k = 16 layout only")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -143,8 +148,10 @@ def main():
     pack = bmm.pack_operand_kmajor if args.kmajor else bmm.pack_operand
     C = None if inp["c_tensor"] is None else torch.from_numpy(inp["c_tensor"]).to(dev)
     c = float(inp["c_scalar"])
-    A = torch.empty((w.batch, w.M_rep, w.K_rep, 16, 8), dtype=torch.int32, device=dev)
-    B = torch.empty((w.batch, w.N_rep, w.K_rep, 8, 8), dtype=torch.int32, device=dev)
+    ka = args.atom_k
+    A = torch.empty((w.batch, w.M_rep, w.K // ka, 16, ka // 2), dtype=torch.int32, device=dev)
+    B = torch.empty((w.batch, w.N_rep, w.K // ka, 8, ka // 2), dtype=torch.int32, device=dev)
+    pack_kw = {} if ka == 16 else {"atom_k": ka}
     D = torch.empty((w.batch, w.M_rep, w.N_rep, 16, 8), dtype=torch.float32, device=dev)
     kernel = bmm.select_kernel(w.batch, w.M_rep, w.N_rep, w.K_rep) if args.kernel == "auto" \
         else args.kernel
@@ -153,10 +160,10 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        pack(a, 16, out=A)
+        pack(a, 16, out=A, **pack_kw)
         if ev is not None:
             ev[1].record(stream)
-        pack(b, 8, out=B)
+        pack(b, 8, out=B, **pack_kw)
         if ev is not None:
             ev[2].record(stream)
         bmm.mma_tile(A, B, C, c, w.dtype, out=D, kernel=kernel, alpha=args.alpha, beta=args.beta)
@@ -219,7 +226,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
                    "c": "tensor" if w.c_tensor else "scalar", "kernel": kernel,
-                   "alpha": args.alpha, "beta": args.beta,
+                   "alpha": args.alpha, "beta": args.beta, "atom_k": ka,
                    "step": ("pack_kmajor A + pack_kmajor B + mma_tile" if args.kmajor
                             else "pack A + pack B + mma_tile")},
         "roofline": roofline,

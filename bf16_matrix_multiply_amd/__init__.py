@@ -12,7 +12,9 @@ coordinates and ownership"):
     A packed: (batch, M/16, K/16, 16, 8) 32-bit words
     B packed: (batch, N/8,  K/16,  8, 8) 32-bit words
     C, D:     (batch, M/16, N/8,  16, 8) float32
-Packed words are held in int32 tensors (bit containers).
+or, with an atom K of 8 (the m16n8k8 form), A (batch, M/16, K/8, 16, 4) and
+B (batch, N/8, K/8, 8, 4). Packed words are held in int32 tensors (bit
+containers).
 """
 from __future__ import annotations
 
@@ -22,7 +24,7 @@ import os
 import torch
 
 __all__ = ["BmmError", "pack_operand", "pack_operand_kmajor", "box_copy", "mma_tile", "select_kernel",
-           "library_path", "KERNELS"]
+           "library_path", "KERNELS", "MmaOpts"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbmm.so")
@@ -55,6 +57,16 @@ class BoxDesc(ctypes.Structure):
     ]
 
 
+class MmaOpts(ctypes.Structure):
+    _fields_ = [
+        ("atom_k", ctypes.c_int32),
+        ("kernel", ctypes.c_int32),
+        ("scaled", ctypes.c_int32),
+        ("alpha", ctypes.c_float),
+        ("beta", ctypes.c_float),
+    ]
+
+
 _lib = None
 
 
@@ -76,6 +88,9 @@ def lib():
         L.bmm_last_error.restype = ctypes.c_char_p
         L.bmm_pack_operand.argtypes = [p, p, i64, i64, i64, i64, i32, p]
         L.bmm_pack_operand_kmajor.argtypes = [p, p, i64, i64, i64, i64, i32, p]
+        L.bmm_pack_operand_k8.argtypes = [p, p, i64, i64, i64, i64, i32, p]
+        L.bmm_mma_tile_opts.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64, i64,
+                                        ctypes.c_int, ctypes.POINTER(MmaOpts), p]
         L.bmm_box_copy.argtypes = [p, p, ctypes.POINTER(BoxDesc), ctypes.POINTER(i64), p]
         L.bmm_mma_tile.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64, i64, ctypes.c_int,
                                    p]
@@ -84,8 +99,9 @@ def lib():
         L.bmm_mma_tile_scaled.argtypes = [p, p, p, p, ctypes.c_float, ctypes.c_float,
                                           ctypes.c_float, i64, i64, i64, i64, ctypes.c_int, i32, p]
         L.bmm_select_kernel.argtypes = [i64, i64, i64, i64]
-        for f in (L.bmm_pack_operand, L.bmm_pack_operand_kmajor, L.bmm_box_copy, L.bmm_mma_tile, L.bmm_mma_tile_with, L.bmm_mma_tile_scaled,
-                  L.bmm_select_kernel):
+        for f in (L.bmm_pack_operand, L.bmm_pack_operand_kmajor, L.bmm_pack_operand_k8,
+                  L.bmm_box_copy, L.bmm_mma_tile, L.bmm_mma_tile_with, L.bmm_mma_tile_scaled,
+                  L.bmm_mma_tile_opts, L.bmm_select_kernel):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -114,12 +130,15 @@ def _require_cuda(*ts):
 
 
 def pack_operand(x: torch.Tensor, atom_rows: int, K: int | None = None,
-                 out: torch.Tensor | None = None) -> torch.Tensor:
+                 out: torch.Tensor | None = None, atom_k: int = 16) -> torch.Tensor:
     """Row-major (batch, rows, ld) or (rows, ld) 16-bit tensor -> packed words
-    (batch, rows/R, K/16, R, 8) int32 (R = atom_rows: 16 for A, 8 for B).
+    (batch, rows/R, K/atom_k, R, atom_k/2) int32 (R = atom_rows: 16 for A, 8
+    for B; atom_k 16, or 8 for bmm_pack_operand_k8).
 
     The source must have unit innermost stride and rows ``ld`` elements apart,
     with batches ``rows * ld`` apart; K (default ld) may be smaller than ld."""
+    if atom_k not in (16, 8):
+        raise ValueError("pack_operand: atom_k must be 16 or 8")
     _require_cuda(x)
     if x.element_size() != 2:
         raise ValueError("pack_operand takes 16-bit (f16/bf16 bit) tensors")
@@ -130,13 +149,13 @@ def pack_operand(x: torch.Tensor, atom_rows: int, K: int | None = None,
             (batch > 1 and x.stride(0) != rows * ld):
         raise ValueError("pack_operand: source must be (batch, rows, ld) with dense strides")
     K = ld if K is None else K
-    shape = (batch, rows // atom_rows, K // 16, atom_rows, 8)
+    shape = (batch, rows // atom_rows, K // atom_k, atom_rows, atom_k // 2)
     if out is None:
         out = torch.empty(shape, dtype=torch.int32, device=x.device)
     elif tuple(out.shape) != shape or not out.is_contiguous() or out.element_size() != 4:
         raise ValueError(f"pack_operand: out must be a contiguous 32-bit tensor of shape {shape}")
-    _check(lib().bmm_pack_operand(_ptr(out), _ptr(x), batch, rows, K, ld, atom_rows,
-                                  _stream(x)))
+    fn = lib().bmm_pack_operand if atom_k == 16 else lib().bmm_pack_operand_k8
+    _check(fn(_ptr(out), _ptr(x), batch, rows, K, ld, atom_rows, _stream(x)))
     return out
 
 
@@ -204,11 +223,15 @@ def mma_tile(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None,
     C is a float32 tensor in D's layout or None (then every element starts
     from the scalar ``c``). ``out`` may be C itself (in place). With alpha or
     beta given, the alpha/beta form runs instead (bmm_mma_tile_scaled):
-    D = fma(alpha, A * B^T, beta * C), the product accumulated from zero."""
+    D = fma(alpha, A * B^T, beta * C), the product accumulated from zero.
+    Operands packed with an atom K of 8 ((..., 16, 4) and (..., 8, 4) words)
+    go through bmm_mma_tile_opts with atom_k = 8."""
     _require_cuda(A, B, C, out)
-    if A.dim() != 5 or B.dim() != 5 or A.shape[3:] != (16, 8) or B.shape[3:] != (8, 8):
-        raise ValueError("mma_tile: A must be (batch, M_rep, K_rep, 16, 8) and B "
-                         "(batch, N_rep, K_rep, 8, 8) packed words")
+    if A.dim() != 5 or B.dim() != 5 or A.shape[3] != 16 or B.shape[3] != 8 or \
+            A.shape[4] not in (8, 4) or B.shape[4] != A.shape[4]:
+        raise ValueError("mma_tile: A must be (batch, M_rep, K_rep, 16, w) and B "
+                         "(batch, N_rep, K_rep, 8, w) packed words, w = 8 (k = 16) or 4 (k = 8)")
+    atom_k = 2 * A.shape[4]
     batch, M_rep, K_rep = A.shape[:3]
     if B.shape[0] != batch or B.shape[2] != K_rep:
         raise ValueError("mma_tile: A and B disagree on batch or K_rep")
@@ -224,7 +247,14 @@ def mma_tile(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None,
         out = torch.empty(shape, dtype=torch.float32, device=A.device)
     elif tuple(out.shape) != shape or out.dtype != torch.float32 or not out.is_contiguous():
         raise ValueError(f"mma_tile: out must be a contiguous float32 tensor of shape {shape}")
-    if alpha is None and beta is None:
+    if atom_k == 8:
+        scaled = not (alpha is None and beta is None)
+        opts = MmaOpts(8, KERNELS[kernel], int(scaled), 1.0 if alpha is None else float(alpha),
+                       1.0 if beta is None else float(beta))
+        _check(lib().bmm_mma_tile_opts(_ptr(out), _ptr(A), _ptr(B), _ptr(C), float(c), batch,
+                                       M_rep, N_rep, K_rep, _DTYPES[dtype], ctypes.byref(opts),
+                                       _stream(A)))
+    elif alpha is None and beta is None:
         _check(lib().bmm_mma_tile_with(_ptr(out), _ptr(A), _ptr(B), _ptr(C), float(c), batch,
                                        M_rep, N_rep, K_rep, _DTYPES[dtype], KERNELS[kernel],
                                        _stream(A)))

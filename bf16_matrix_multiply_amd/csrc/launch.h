@@ -20,17 +20,31 @@ struct MmaArgs {
   // D = fma(alpha, acc, beta * C) (C or c_scalar) in the epilogue.
   int scaled;
   float alpha, beta;
+  // atom K of the packed operands: 16 (m16n8k16 layout) or 8 (m16n8k8)
+  int atom_k;
 };
 
+// In 8-value K chunks, one 32-deep MFMA step spans the same bytes in either
+// layout (A: 64 words per chunk per 16-row atom block, B: 32 words per 8-row
+// block); only a lane's offset inside the step differs. Lane group g takes
+// chunk g of the step: atom g/2, half g%2 for k = 16; atom g for k = 8.
+__host__ __device__ inline int64_t k_chunks(const MmaArgs& a) { return a.K_rep * (a.atom_k / 8); }
+__device__ inline int a_lane_words(int atom_k, int row, int g) {
+  return atom_k == 16 ? (g >> 1) * 128 + row * 8 + (g & 1) * 4 : g * 64 + row * 4;
+}
+__device__ inline int b_lane_words(int atom_k, int row, int g) {
+  return atom_k == 16 ? (g >> 1) * 64 + row * 8 + (g & 1) * 4 : g * 32 + row * 4;
+}
+
 hipError_t launch_pack(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
-                       int64_t K, int64_t ld, int R, hipStream_t s);
+                       int64_t K, int64_t ld, int R, int atom_k, hipStream_t s);
 hipError_t launch_pack_kmajor(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
                               int64_t K, int64_t ld, int R, hipStream_t s);
 hipError_t launch_box(void* dst, const void* src, const bmm_box_desc& d, hipStream_t s);
 hipError_t launch_mma_direct(const MmaArgs& a, hipStream_t s);
 // The tiled kernel addresses one tile's operands with 32-bit buffer offsets:
-// it takes K_rep < 2^18 (K < 4M).
-constexpr int64_t kTiledMaxKRep = int64_t(1) << 18;
+// it takes K < 2^22.
+constexpr int64_t kTiledMaxK = int64_t(1) << 22;
 hipError_t launch_mma_tiled(const MmaArgs& a, hipStream_t s);
 hipError_t launch_mma_skinny(const MmaArgs& a, hipStream_t s);
 

@@ -15,8 +15,9 @@
 // D[m = l%16][n = 4*(l/16) .. 4*(l/16)+3], which in the accumulator layout is
 // one contiguous 16-byte piece of N atom (l/16)/2. Lane group g = l/16 takes K
 // values 8g .. 8g+7 of the step for both operands: K atom g/2, words
-// 4*(g%2) .. 4*(g%2)+3. A's 16-row fragment for a step is then 1 KB of
-// contiguous memory, and every lane moves exactly 16 bytes.
+// 4*(g%2) .. 4*(g%2)+3 (or K atom g, all 4 words, in the k = 8 layout). A's
+// 16-row fragment for a step is then 1 KB of contiguous memory, and every
+// lane moves exactly 16 bytes.
 #include "common.h"
 #include "launch.h"
 
@@ -52,29 +53,30 @@ __global__ __launch_bounds__(kDirectWaves* kWave) void mma_direct_kernel(MmaArgs
   }
 
   // Operand fragments: A row m, B row n = lane % 16 of this tile's 16 columns.
-  const uint32_t* a_ptr = p.A + (bm * p.K_rep) * kAtomWordsA + m * 8 + 4 * (g & 1);
+  const int64_t nck = k_chunks(p);
+  const uint32_t* a_ptr = p.A + bm * nck * 64 + a_lane_words(p.atom_k, m, g);
   const int64_t nb = 2 * nt + (m >> 3);
   const bool b_ok = nb < p.N_rep;
   const uint32_t* b_ptr =
-      p.B + ((b * p.N_rep + (b_ok ? nb : 0)) * p.K_rep) * kAtomWordsB + (m & 7) * 8 + 4 * (g & 1);
+      p.B + (b * p.N_rep + (b_ok ? nb : 0)) * nck * 32 + b_lane_words(p.atom_k, m & 7, g);
   const u32x4 zero = {0u, 0u, 0u, 0u};
 
-  const int64_t steps = (p.K_rep + 1) / 2;
+  const int64_t steps = (nck + 3) / 4;
   int64_t s = 0;
   // Two steps per iteration keep two loads of each operand in flight.
   for (; s + 2 <= steps; s += 2) {
-    const int64_t kr0 = 2 * s + (g >> 1), kr1 = kr0 + 2;
-    const u32x4 a0 = kr0 < p.K_rep ? load16(a_ptr + kr0 * kAtomWordsA) : zero;
-    const u32x4 a1 = kr1 < p.K_rep ? load16(a_ptr + kr1 * kAtomWordsA) : zero;
-    const u32x4 b0 = (b_ok && kr0 < p.K_rep) ? load16(b_ptr + kr0 * kAtomWordsB) : zero;
-    const u32x4 b1 = (b_ok && kr1 < p.K_rep) ? load16(b_ptr + kr1 * kAtomWordsB) : zero;
+    const bool k0 = 4 * s + g < nck, k1 = 4 * s + 4 + g < nck;
+    const u32x4 a0 = k0 ? load16(a_ptr + s * 256) : zero;
+    const u32x4 a1 = k1 ? load16(a_ptr + s * 256 + 256) : zero;
+    const u32x4 b0 = (b_ok && k0) ? load16(b_ptr + s * 128) : zero;
+    const u32x4 b1 = (b_ok && k1) ? load16(b_ptr + s * 128 + 128) : zero;
     acc = mfma_16x16x32<DT>(b0, a0, acc);
     acc = mfma_16x16x32<DT>(b1, a1, acc);
   }
   for (; s < steps; ++s) {
-    const int64_t kr = 2 * s + (g >> 1);
-    const u32x4 a0 = kr < p.K_rep ? load16(a_ptr + kr * kAtomWordsA) : zero;
-    const u32x4 b0 = (b_ok && kr < p.K_rep) ? load16(b_ptr + kr * kAtomWordsB) : zero;
+    const bool k0 = 4 * s + g < nck;
+    const u32x4 a0 = k0 ? load16(a_ptr + s * 256) : zero;
+    const u32x4 b0 = (b_ok && k0) ? load16(b_ptr + s * 128) : zero;
     acc = mfma_16x16x32<DT>(b0, a0, acc);
   }
   if (!n_ok) return;

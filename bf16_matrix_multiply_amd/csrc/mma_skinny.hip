@@ -39,19 +39,19 @@ __global__ __launch_bounds__(kWaves* kWave) void mma_skinny_kernel(MmaArgs p) {
   const int64_t mg = blockIdx.y;                 // group of MR M atoms
   const int64_t b = blockIdx.z;
   const int m = lane & 15, g = lane >> 4;
-  const int64_t K_rep = p.K_rep;
   const int64_t m_atom0 = mg * MR;
 
   // ---- fragment pointers ----
   // B block nb: rows n = 16*nb + lane%16 of this tile -> atom 2*nb + m/8, row m%8.
+  const int64_t nck = k_chunks(p);   // 8-value K chunks; a step covers 4
   const uint32_t* b_ptr[kNBlocks];
   bool b_ok[kNBlocks];
 #pragma unroll
   for (int nb = 0; nb < kNBlocks; ++nb) {
     const int64_t atom = nt * kNAtoms + 2 * nb + (m >> 3);
     b_ok[nb] = atom < p.N_rep;
-    b_ptr[nb] = p.B + ((b * p.N_rep + (b_ok[nb] ? atom : 0)) * K_rep) * kAtomWordsB +
-                (m & 7) * 8 + 4 * (g & 1);
+    b_ptr[nb] = p.B + (b * p.N_rep + (b_ok[nb] ? atom : 0)) * nck * 32 +
+                b_lane_words(p.atom_k, m & 7, g);
   }
   const uint32_t* a_ptr[MR];
   bool a_ok[MR];
@@ -59,12 +59,11 @@ __global__ __launch_bounds__(kWaves* kWave) void mma_skinny_kernel(MmaArgs p) {
   for (int mi = 0; mi < MR; ++mi) {
     const int64_t atom = m_atom0 + mi;
     a_ok[mi] = atom < p.M_rep;
-    a_ptr[mi] = p.A + ((b * p.M_rep + (a_ok[mi] ? atom : 0)) * K_rep) * kAtomWordsA + m * 8 +
-                4 * (g & 1);
+    a_ptr[mi] = p.A + (b * p.M_rep + (a_ok[mi] ? atom : 0)) * nck * 64 + a_lane_words(p.atom_k, m, g);
   }
 
   // ---- this wave's K steps ----
-  const int64_t steps = (K_rep + 1) / 2;
+  const int64_t steps = (nck + 3) / 4;
   const int64_t chunk = (steps + W - 1) / W;
   const int64_t s_begin = wave * chunk < steps ? wave * chunk : steps;
   const int64_t s_end = s_begin + chunk < steps ? s_begin + chunk : steps;
@@ -92,18 +91,17 @@ __global__ __launch_bounds__(kWaves* kWave) void mma_skinny_kernel(MmaArgs p) {
 
   const u32x4 zero = {0u, 0u, 0u, 0u};
   int64_t s = s_begin;
-  // Full groups: every K atom is inside K_rep (the ragged step is the last one).
-  for (; s + kUnroll <= s_end && 2 * (s + kUnroll) <= K_rep; s += kUnroll) {
+  // Full groups: every K chunk is inside K (the ragged step is the last one).
+  for (; s + kUnroll <= s_end && 4 * (s + kUnroll) <= nck; s += kUnroll) {
     u32x4 bf[kUnroll][kNBlocks], af[kUnroll][MR];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t kr = 2 * (s + u) + (g >> 1);
 #pragma unroll
       for (int nb = 0; nb < kNBlocks; ++nb)
-        bf[u][nb] = b_ok[nb] ? load16_nt(b_ptr[nb] + kr * kAtomWordsB) : zero;
+        bf[u][nb] = b_ok[nb] ? load16_nt(b_ptr[nb] + (s + u) * 128) : zero;
 #pragma unroll
       for (int mi = 0; mi < MR; ++mi)
-        af[u][mi] = a_ok[mi] ? load16(a_ptr[mi] + kr * kAtomWordsA) : zero;
+        af[u][mi] = a_ok[mi] ? load16(a_ptr[mi] + (s + u) * 256) : zero;
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
@@ -115,15 +113,14 @@ __global__ __launch_bounds__(kWaves* kWave) void mma_skinny_kernel(MmaArgs p) {
   }
   // Remaining steps one at a time, with the K tail zeroed in registers.
   for (; s < s_end; ++s) {
-    const int64_t kr = 2 * s + (g >> 1);
-    const bool k_ok = kr < K_rep;
+    const bool k_ok = 4 * s + g < nck;
     u32x4 bf[kNBlocks], af[MR];
 #pragma unroll
     for (int nb = 0; nb < kNBlocks; ++nb)
-      bf[nb] = (k_ok && b_ok[nb]) ? load16_nt(b_ptr[nb] + kr * kAtomWordsB) : zero;
+      bf[nb] = (k_ok && b_ok[nb]) ? load16_nt(b_ptr[nb] + s * 128) : zero;
 #pragma unroll
     for (int mi = 0; mi < MR; ++mi)
-      af[mi] = (k_ok && a_ok[mi]) ? load16(a_ptr[mi] + kr * kAtomWordsA) : zero;
+      af[mi] = (k_ok && a_ok[mi]) ? load16(a_ptr[mi] + s * 256) : zero;
 #pragma unroll
     for (int mi = 0; mi < MR; ++mi)
 #pragma unroll

@@ -124,7 +124,7 @@ __device__ __forceinline__ TileCoord tile_of(int64_t w, int64_t n_tiles, int64_t
   return c;
 }
 
-template <int DT, bool kHasC, bool kScaled>
+template <int DT, int KA, bool kHasC, bool kScaled>
 __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64_t n_tiles,
                                                                int64_t MT, int64_t NT) {
   // Four separate objects (not one array) so that the compiler can tell the
@@ -136,41 +136,48 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
   const int wm = wave >> 2, wn = wave & 3;
   const TileCoord tc = tile_of(blockIdx.x, n_tiles, MT, NT);
   const int64_t m_atom0 = tc.mt * kTileMAtoms, n_atom0 = tc.nt * kTileNAtoms;
-  const int64_t K_rep = p.K_rep;
 
   // ---- direct-to-LDS staging ----
-  // Wave w loads A fragments f = 8r + w (row block f / 2, K atom f % 2 = w % 2)
-  // and B fragments likewise. Lane l of an A fragment fetches row l % 16 of M
-  // atom 2 * (f / 2) + (l / 16) % 2, half l / 32; lane l of a B fragment
-  // fetches row l % 8 of N atom 4 * (f / 2) + (l / 8) % 4, half l / 32.
+  // Wave w loads A fragments f = 8r + w (row block f / 2, 16-deep half f % 2 =
+  // w % 2 of the slab) and B fragments likewise. Lane l of an A fragment
+  // fetches row l % 16 of M atom 2 * (f / 2) + (l / 16) % 2, and of a B
+  // fragment row l % 8 of N atom 4 * (f / 2) + (l / 8) % 4; in both, the 8 K
+  // values of chunk cs = 2 * (f % 2) + l / 32 of the slab's four 8-value
+  // chunks (k = 16 layout: atom cs / 2, half cs % 2; k = 8 layout: atom cs).
   const int kj = wave & 1;
-  const int64_t a_row_bytes = K_rep * 512, b_row_bytes = K_rep * 256;
+  const int cs = 2 * kj + (lane >> 5);
+  const int64_t nck = k_chunks(p);
+  const int64_t a_row_bytes = nck * 256, b_row_bytes = nck * 128;
   const int64_t a_left = (p.M_rep - m_atom0) * a_row_bytes;
   const int64_t b_left = (p.N_rep - n_atom0) * b_row_bytes;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(p.A + (tc.b * p.M_rep + m_atom0) * K_rep * kAtomWordsA), 0,
+      const_cast<uint32_t*>(p.A + (tc.b * p.M_rep + m_atom0) * nck * 64), 0,
       int(a_left < kOutOfRange ? a_left : kOutOfRange), kBufferFlags);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(p.B + (tc.b * p.N_rep + n_atom0) * K_rep * kAtomWordsB), 0,
+      const_cast<uint32_t*>(p.B + (tc.b * p.N_rep + n_atom0) * nck * 32), 0,
       int(b_left < kOutOfRange ? b_left : kOutOfRange), kBufferFlags);
   uint32_t a_voff[kLoadsA], b_voff[kLoadsB];
 #pragma unroll
   for (int r = 0; r < kLoadsA; ++r) {
     const int blk = (kWaves * r + wave) >> 1;
-    a_voff[r] = uint32_t((2 * blk + ((lane >> 4) & 1)) * a_row_bytes + kj * 512 +
-                         (lane & 15) * 32 + (lane >> 5) * 16);
+    a_voff[r] = uint32_t((2 * blk + ((lane >> 4) & 1)) * a_row_bytes +
+                         (KA == 16 ? kj * 512 + (lane & 15) * 32 + (lane >> 5) * 16
+                                         : cs * 256 + (lane & 15) * 16));
   }
 #pragma unroll
   for (int r = 0; r < kLoadsB; ++r) {
     const int blk = (kWaves * r + wave) >> 1;
-    b_voff[r] = uint32_t((4 * blk + ((lane >> 3) & 3)) * b_row_bytes + kj * 256 +
-                         (lane & 7) * 32 + (lane >> 5) * 16);
+    b_voff[r] = uint32_t((4 * blk + ((lane >> 3) & 3)) * b_row_bytes +
+                         (KA == 16 ? kj * 256 + (lane & 7) * 32 + (lane >> 5) * 16
+                                         : cs * 128 + (lane & 7) * 16));
   }
 
-  // Loads of slab k into stage st (slabs past K_rep, and K atoms past it, read 0).
+  // Loads of slab k into stage st (slabs past the end, and K chunks past it,
+  // read 0). With k = 16 atoms both halves of an atom are valid together, so
+  // the test is uniform over the wave.
   auto issue = [&](Stage& st, int64_t k) {
-    const uint32_t koff_a = uint32_t(k * kSlabKAtoms * 512), koff_b = uint32_t(k * kSlabKAtoms * 256);
-    const bool k_ok = k * kSlabKAtoms + kj < K_rep;
+    const uint32_t koff_a = uint32_t(k * 1024), koff_b = uint32_t(k * 512);
+    const bool k_ok = KA == 16 ? 4 * k + 2 * kj < nck : 4 * k + cs < nck;
 #pragma unroll
     for (int r = 0; r < kLoadsA; ++r)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -291,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kWaveBlocksM * kWaveBlocksN - kLoadsPerSlab, 0);
   };
-  const int64_t n_slabs = (K_rep + kSlabKAtoms - 1) / kSlabKAtoms;
+  const int64_t n_slabs = (nck + 3) / 4;
   for (int64_t s = 0; s < n_slabs; s += kStages) {
     slab(s + 0, st0, st1, fb[0], fa[0], fb[1], fa[1]);
     slab(s + 1, st1, st2, fb[1], fa[1], fb[0], fa[0]);
@@ -334,15 +341,19 @@ hipError_t launch_mma_tiled(const MmaArgs& a, hipStream_t s) {
   const int64_t n_tiles = a.batch * MT * NT;
   if (n_tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
   // Buffer offsets inside one tile's 16 A atom rows must stay below 2^31.
-  if (a.K_rep >= kTiledMaxKRep) return hipErrorInvalidValue;
-  auto pick = [&](auto dt) {
-    constexpr int D = decltype(dt)::value;
+  if (k_chunks(a) * 8 >= kTiledMaxK) return hipErrorInvalidValue;
+  auto pick = [&](auto dt, auto ka) {
+    constexpr int D = decltype(dt)::value, KA = decltype(ka)::value;
     if (a.scaled)
-      return a.C ? mma_tiled_kernel<D, true, true> : mma_tiled_kernel<D, false, true>;
-    return a.C ? mma_tiled_kernel<D, true, false> : mma_tiled_kernel<D, false, false>;
+      return a.C ? mma_tiled_kernel<D, KA, true, true> : mma_tiled_kernel<D, KA, false, true>;
+    return a.C ? mma_tiled_kernel<D, KA, true, false> : mma_tiled_kernel<D, KA, false, false>;
   };
-  auto kern = a.dtype == kBF16 ? pick(std::integral_constant<int, kBF16>{})
-                               : pick(std::integral_constant<int, kF16>{});
+  auto pick_ka = [&](auto dt) {
+    return a.atom_k == 16 ? pick(dt, std::integral_constant<int, 16>{})
+                          : pick(dt, std::integral_constant<int, 8>{});
+  };
+  auto kern = a.dtype == kBF16 ? pick_ka(std::integral_constant<int, kBF16>{})
+                               : pick_ka(std::integral_constant<int, kF16>{});
   hipLaunchKernelGGL(kern, dim3(unsigned(n_tiles)), dim3(kThreads), 0, s, a, n_tiles, MT, NT);
   return hipGetLastError();
 }

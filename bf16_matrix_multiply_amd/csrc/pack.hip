@@ -6,7 +6,8 @@
 // packed words of half an atom row (even K in the low half of each word on
 // this little-endian machine), so packing is a permutation of 16-byte chunks:
 // output chunk (row block rb, c) with c = (kr, i, h) comes from source row
-// R*rb + i, K offset 16*kr + 8*h. Stores are fully contiguous; each 32-byte
+// R*rb + i, K offset 16*kr + 8*h (with an atom K of 8: c = (kr, i), K offset
+// 8*kr). Stores are fully contiguous; each 32-byte
 // piece of a source row is read by two adjacent lanes, and the K atoms of one
 // row are read by the same block in successive chunk groups.
 #include "common.h"
@@ -18,7 +19,7 @@ namespace {
 constexpr int kPackThreads = 256;
 constexpr int kPackUnroll = 4;
 
-template <int R>
+template <int R, int KA>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(uint32_t* __restrict__ dst,
                                                             const uint16_t* __restrict__ src,
                                                             int64_t rb0, int32_t chunks_per_rb,
@@ -33,8 +34,10 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(uint32_t* __restrict
   for (int u = 0; u < kPackUnroll; ++u) {
     const int32_t c = c0 + u * kPackThreads;
     if (c < chunks_per_rb) {
-      const int32_t h = c & 1, i = (c >> 1) & (R - 1), kr = c >> (kLog2R + 1);
-      v[u] = load16_nt(reinterpret_cast<const uint32_t*>(srow + i * ld + 16 * kr + 8 * h));
+      // chunk c: K atom, row in atom, half (k = 16) or K atom, row (k = 8)
+      const int32_t i = KA == 16 ? (c >> 1) & (R - 1) : c & (R - 1);
+      const int32_t k8 = KA == 16 ? 2 * (c >> (kLog2R + 1)) + (c & 1) : c >> kLog2R;
+      v[u] = load16_nt(reinterpret_cast<const uint32_t*>(srow + i * ld + 8 * k8));
     }
   }
 #pragma unroll
@@ -107,19 +110,16 @@ hipError_t launch_pack_kmajor(uint32_t* dst, const uint16_t* src, int64_t batch,
 }
 
 hipError_t launch_pack(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
-                       int64_t K, int64_t ld, int R, hipStream_t s) {
+                       int64_t K, int64_t ld, int R, int atom_k, hipStream_t s) {
   const int64_t n_rb = batch * (rows / R);
-  const int32_t chunks = int32_t(2 * R * (K / 16));  // 16-byte chunks per row block
+  const int32_t chunks = int32_t(R * (K / 8));  // 16-byte chunks per row block
   const int per_block = kPackThreads * kPackUnroll;
   const unsigned gx = unsigned((chunks + per_block - 1) / per_block);
   for (int64_t rb0 = 0; rb0 < n_rb; rb0 += 65535) {
     const unsigned gy = unsigned(n_rb - rb0 < 65535 ? n_rb - rb0 : 65535);
-    if (R == 16)
-      hipLaunchKernelGGL(pack_kernel<16>, dim3(gx, gy), dim3(kPackThreads), 0, s, dst, src,
-                         rb0, chunks, ld);
-    else
-      hipLaunchKernelGGL(pack_kernel<8>, dim3(gx, gy), dim3(kPackThreads), 0, s, dst, src,
-                         rb0, chunks, ld);
+    auto kern = R == 16 ? (atom_k == 16 ? pack_kernel<16, 16> : pack_kernel<16, 8>)
+                        : (atom_k == 16 ? pack_kernel<8, 16> : pack_kernel<8, 8>);
+    hipLaunchKernelGGL(kern, dim3(gx, gy), dim3(kPackThreads), 0, s, dst, src, rb0, chunks, ld);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -40,7 +40,7 @@ int64_t mul_capped(std::initializer_list<int64_t> xs) {
 }  // namespace
 
 Status check_pack(const uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
-                  int64_t K, int64_t ld_src, int32_t atom_rows) {
+                  int64_t K, int64_t ld_src, int32_t atom_rows, int32_t atom_k) {
   if (atom_rows != 16 && atom_rows != 8)
     return fail(BMM_EINVAL, "pack_operand: atom_rows must be 16 (A) or 8 (B), got %lld",
                 atom_rows);
@@ -51,7 +51,8 @@ Status check_pack(const uint32_t* dst, const uint16_t* src, int64_t batch, int64
   if (rows % atom_rows)
     return fail(BMM_EINVAL, "pack_operand: rows (%lld) is not a multiple of atom_rows (%lld)",
                 rows, atom_rows);
-  if (K % 16) return fail(BMM_EINVAL, "pack_operand: K (%lld) is not a multiple of 16", K);
+  if (K % atom_k)
+    return fail(BMM_EINVAL, "pack_operand: K (%lld) is not a multiple of %lld", K, atom_k);
   if (ld_src < K) return fail(BMM_EINVAL, "pack_operand: ld_src (%lld) < K (%lld)", ld_src, K);
   if (ld_src > (int64_t(1) << 32)) return fail(BMM_EINVAL, "pack_operand: ld_src too large");
   if (batch == 0 || rows == 0 || K == 0) return Status{};
@@ -157,7 +158,9 @@ Status check_box(const void* dst, const void* src, const bmm_box_desc* d) {
 
 Status check_mma(const float* D, const uint32_t* A, const uint32_t* B, const float* C,
                  int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep, int32_t dtype,
-                 int32_t kernel) {
+                 int32_t kernel, int32_t atom_k) {
+  if (atom_k != 16 && atom_k != 8)
+    return fail(BMM_EINVAL, "mma_tile: atom_k must be 16 or 8, got %lld", atom_k);
   if (dtype != BMM_F16 && dtype != BMM_BF16)
     return fail(BMM_EINVAL, "mma_tile: dtype %lld is neither BMM_F16 nor BMM_BF16", dtype);
   if (kernel < BMM_KERNEL_AUTO || kernel > BMM_KERNEL_SKINNY)
@@ -167,8 +170,9 @@ Status check_mma(const float* D, const uint32_t* A, const uint32_t* B, const flo
   if (batch > kMaxExtent || M_rep > kMaxExtent || N_rep > kMaxExtent || K_rep > (1 << 26))
     return fail(BMM_EINVAL, "mma_tile: extent too large");
   const int64_t d_bytes = mul_capped({batch, M_rep, N_rep, 512});
-  const int64_t a_bytes = mul_capped({batch, M_rep, K_rep, 512});
-  const int64_t b_bytes = mul_capped({batch, N_rep, K_rep, 256});
+  // one atom: 16 (A) or 8 (B) rows of atom_k / 2 words
+  const int64_t a_bytes = mul_capped({batch, M_rep, K_rep, 32 * atom_k});
+  const int64_t b_bytes = mul_capped({batch, N_rep, K_rep, 16 * atom_k});
   if (d_bytes < 0 || a_bytes < 0 || b_bytes < 0) return fail(BMM_EINVAL, "mma_tile: too large");
   if (d_bytes == 0) return Status{};
   if (!D) return fail(BMM_EINVAL, "mma_tile: D is null");

@@ -16,7 +16,7 @@ struct Status {
 };
 
 Status check_pack(const uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
-                  int64_t K, int64_t ld_src, int32_t atom_rows);
+                  int64_t K, int64_t ld_src, int32_t atom_rows, int32_t atom_k);
 
 Status check_pack_kmajor(const uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
                          int64_t K, int64_t ld_src, int32_t atom_rows);
@@ -25,7 +25,7 @@ Status check_box(const void* dst, const void* src, const bmm_box_desc* d);
 
 Status check_mma(const float* D, const uint32_t* A, const uint32_t* B, const float* C,
                  int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep, int32_t dtype,
-                 int32_t kernel);
+                 int32_t kernel, int32_t atom_k);
 
 // Largest image (bytes) one box repeat may stage through LDS.
 constexpr int64_t kBoxImageLimit = 65536;

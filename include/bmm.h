@@ -77,6 +77,25 @@ int bmm_pack_operand(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t 
                      int64_t K, int64_t ld_src, int32_t atom_rows, void* stream);
 
 /*
+ * bmm_pack_operand_k8 — row-major halves to packed atoms with an atom K of 8.
+ *
+ * The mma.sync page's introduction names the m16n8k8 form beside m16n8k16,
+ * and its table of shapes gives k = 8 for f16/bf16 inputs. With k = 8 the
+ * layouts of "Operand coordinates and ownership" hold k/2 = 4 words per atom
+ * row: A is (M_repeat, K_repeat, 16, 4) and B is (N_repeat, K_repeat, 8, 4)
+ * words, K_repeat = K/8:
+ *
+ *   dst[b, r, kr, i, w] = src[b, R*r+i, 8*kr+2*w] | src[b, R*r+i, 8*kr+2*w+1] << 16
+ *
+ * dst  (batch, rows/R, K/8, R, 4) uint32, contiguous, 16-byte aligned.
+ * K    a multiple of 8. Every other argument, and the errors, as
+ *      bmm_pack_operand.
+ * The result feeds bmm_mma_tile_opts with atom_k = 8.
+ */
+int bmm_pack_operand_k8(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
+                        int64_t K, int64_t ld_src, int32_t atom_rows, void* stream);
+
+/*
  * bmm_pack_operand_kmajor — packing from a K-major (transposed) source.
  *
  * The mma.sync page ("Accumulation, transpose and alpha/beta") leaves a
@@ -195,7 +214,40 @@ int bmm_mma_tile_scaled(float* D, const uint32_t* A, const uint32_t* B, const fl
                         int64_t N_rep, int64_t K_rep, bmm_dtype dtype, int32_t kernel,
                         void* stream);
 
-/* Which kernel AUTO would run for this shape (a bmm_kernel value), or < 0. */
+/*
+ * bmm_mma_tile_opts — every form of the multiply-accumulate behind one call.
+ *
+ * The options select what the other mma entry points fix:
+ *   atom_k  16: operands in the k = 16 layout (bmm_pack_operand), K_rep
+ *           counts 16-deep atoms; 8: the m16n8k8 layout (bmm_pack_operand_k8,
+ *           the mma.sync page's introduction and table of shapes), A is
+ *           (batch, M_rep, K_rep, 16, 4) and B (batch, N_rep, K_rep, 8, 4)
+ *           words and K_rep counts 8-deep atoms. The sum is the same
+ *           function of the logical operands in both layouts; the hardware
+ *           step stays 32 K values deep.
+ *   kernel  a bmm_kernel value.
+ *   scaled  0: the C-then-D recurrence of bmm_mma_tile; 1: the alpha/beta
+ *           form of bmm_mma_tile_scaled with these alpha and beta (ignored
+ *           when scaled = 0).
+ * opts = NULL means {16, BMM_KERNEL_AUTO, 0, 1, 1}, i.e. bmm_mma_tile.
+ * D, A, B, C, c_scalar, extents, dtype: as bmm_mma_tile.
+ * Errors: as bmm_mma_tile_with; BMM_EINVAL also for atom_k not 16 or 8 and
+ * scaled not 0 or 1.
+ */
+typedef struct {
+  int32_t atom_k;
+  int32_t kernel;
+  int32_t scaled;
+  float alpha;
+  float beta;
+} bmm_mma_opts;
+
+int bmm_mma_tile_opts(float* D, const uint32_t* A, const uint32_t* B, const float* C,
+                      float c_scalar, int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep,
+                      bmm_dtype dtype, const bmm_mma_opts* opts, void* stream);
+
+/* Which kernel AUTO would run for this shape (K_rep in 16-deep atoms; a
+ * bmm_kernel value), or < 0. */
 int bmm_select_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep);
 
 /* Message for the last failed call on this thread ("" if none). */

@@ -192,3 +192,59 @@ def test_pack_kmajor_rejects(L, kw, code, needle):
 def test_pack_kmajor_empty_is_noop(L):
     assert pack_km(L, dst=0, src=0, batch=0) == 0
     assert pack_km(L, dst=0, src=0, K=0) == 0
+
+
+def pack_k8(L, dst=P0, src=P1, batch=1, rows=16, K=24, ld=24, R=16):
+    return L.bmm_pack_operand_k8(dst, src, batch, rows, K, ld, R, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(R=4), EINVAL, "atom_rows"),
+    (dict(K=12, ld=16), EINVAL, "multiple of 8"),
+    (dict(ld=16), EINVAL, "ld_src"),
+    (dict(ld=28), EALIGN, "multiple of 8"),
+    (dict(dst=P0 + 4), EALIGN, "aligned"),
+    (dict(dst=P1 + 64), EOVERLAP, "overlaps"),
+])
+def test_pack_k8_rejects(L, kw, code, needle):
+    assert pack_k8(L, **kw) == code
+    assert needle in err(L)
+
+
+def test_pack_k8_accepts_k_multiple_of_8_only_there(L):
+    # K = 24 is valid for the k = 8 packer (rejected later, on alignment) but
+    # not for the k = 16 one
+    assert pack_k8(L, src=P1 + 2) == EALIGN
+    assert pack(L, K=24, ld=24) == EINVAL and "multiple of 16" in err(L)
+    assert pack_k8(L, dst=0, src=0, K=0, ld=0) == 0
+
+
+def mma_opts(L, D=P0, A=P1, B=P2, C=None, batch=1, M=2, N=3, K=4, dtype=1, opts=None):
+    ref = None if opts is None else ctypes.byref(opts)
+    return L.bmm_mma_tile_opts(D, A, B, C, 0.0, batch, M, N, K, dtype, ref, None)
+
+
+@pytest.mark.parametrize("fields,code,needle", [
+    ((4, 0, 0, 1.0, 1.0), EINVAL, "atom_k"),
+    ((16, 9, 0, 1.0, 1.0), EINVAL, "kernel"),
+    ((8, 0, 2, 1.0, 1.0), EINVAL, "scaled"),
+])
+def test_mma_opts_rejects_fields(L, fields, code, needle):
+    assert mma_opts(L, opts=bmm.MmaOpts(*fields)) == code
+    assert needle in err(L)
+
+
+def test_mma_opts_null_is_plain_call(L):
+    assert mma_opts(L, D=P0 + 4) == EALIGN
+    assert mma_opts(L, D=0, A=0, B=0, M=0) == 0
+
+
+def test_mma_opts_sizes_operands_by_atom_k(L):
+    # A is (1, 2, 4, 16, atom_k/2) words: 4096 bytes with k = 16, 2048 with
+    # k = 8. D placed 3072 bytes into A overlaps it only in the k = 16 layout;
+    # C half-overlapping D then fails the k = 8 call before any launch.
+    D = P1 + 3072
+    k16 = bmm.MmaOpts(16, 1, 0, 1.0, 1.0)
+    k8 = bmm.MmaOpts(8, 1, 0, 1.0, 1.0)
+    assert mma_opts(L, D=D, C=D + 512, opts=k16) == EOVERLAP and "overlaps A" in err(L)
+    assert mma_opts(L, D=D, C=D + 512, opts=k8) == EOVERLAP and "partially overlaps C" in err(L)
