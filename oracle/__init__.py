@@ -32,7 +32,7 @@ CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off"
 def build(force: bool = True) -> str:
     """Compile liboracle.so in place with gcc and return its path."""
     if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
+        tmp = f"{_LIB_PATH}.{os.getpid()}.tmp"
         subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -64,6 +64,12 @@ class Oracle:
                                         ctypes.c_float, i64, i64, i64, i64, ctypes.c_int]
         L.oracle_box_copy.restype = i64
         L.oracle_box_copy.argtypes = [p, p, i32, i32, p, p, p, p, i32, p]
+        L.oracle_box_store.restype = i64
+        L.oracle_box_store.argtypes = [p, p, i32, i32, p, p, p, p, i32, p, i32, i32]
+        L.oracle_mma_splitk.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64, i64, i64,
+                                        i64, ctypes.c_int]
+        L.oracle_mma_splitk_sampled.argtypes = [p, p, i64, p, p, p, ctypes.c_float, i64, i64,
+                                                i64, i64, i64, i64, ctypes.c_int]
         self.L = L
 
     def threads(self) -> int:
@@ -237,6 +243,72 @@ class Oracle:
         return img, int(nbytes)
 
 
+    def _box_args(self, G, box, coords, n_repeat, coord_step, dims, strides):
+        rank = G.ndim if dims is None else len(dims)
+        dims = list(G.shape if dims is None else dims)
+        strides = list(G.strides if strides is None else strides)
+        coord_step = list(coord_step if coord_step is not None else [0] * rank)
+
+        def arr(v, t):
+            a = np.zeros(5, t)
+            a[: len(v)] = v
+            return a
+
+        return rank, (arr(dims, np.int64), arr(strides, np.int64), arr(box, np.int32),
+                      arr(coords, np.int64), arr(coord_step, np.int64))
+
+    def box_store(self, G: np.ndarray, img: np.ndarray, box, coords, n_repeat: int = 1,
+                  coord_step=None, op: str = "store", elem_type: str | None = None,
+                  dims=None, strides=None):
+        """A copy of ``G`` after storing (op="store") or add-reducing (op="add")
+        the (n_repeat, *box) image ``img`` into it; returns (G', bytes).
+
+        elem_type for "add": "f32", "f16", "bf16", "i32" or "i64" (``img`` and
+        ``G`` hold the raw elements: float32, uint16 bits, int32, int64)."""
+        G = np.array(G, copy=True, order="C")
+        img = np.ascontiguousarray(img, dtype=G.dtype)
+        assert img.shape == (n_repeat, *box)
+        rank, (d5, s5, b5, c5, st5) = self._box_args(G, box, coords, n_repeat, coord_step,
+                                                     dims, strides)
+        opc = {"store": 0, "add": 1}[op]
+        et = {None: 0, "f32": 1, "f16": 2, "bf16": 3, "i32": 4, "i64": 5}[elem_type]
+        nbytes = self.L.oracle_box_store(_ptr(G), _ptr(img), rank, G.itemsize, _ptr(d5),
+                                         _ptr(s5), _ptr(b5), _ptr(c5), n_repeat, _ptr(st5),
+                                         opc, et)
+        if nbytes < 0:
+            raise ValueError("oracle_box_store rejected its arguments")
+        return G, int(nbytes)
+
+    def mma_splitk(self, A, B, C, c, dtype, splits: int) -> np.ndarray:
+        """Split-K form over k=16 (A (…,16,8)) or k=8 (A (…,16,4)) operands."""
+        A = np.ascontiguousarray(A, np.uint32)
+        B = np.ascontiguousarray(B, np.uint32)
+        C = None if C is None else np.ascontiguousarray(C, np.float32)
+        batch, M_rep, K_rep = A.shape[:3]
+        N_rep, ka = B.shape[1], 2 * A.shape[4]
+        D = np.empty((batch, M_rep, N_rep, 16, 8), np.float32)
+        rc = self.L.oracle_mma_splitk(_ptr(D), _ptr(A), _ptr(B), _ptr(C), float(c), batch,
+                                      M_rep, N_rep, K_rep, ka, splits, _DTYPES[dtype])
+        if rc != 0:
+            raise ValueError("oracle_mma_splitk rejected its arguments")
+        return D
+
+    def mma_splitk_sampled(self, A, B, C, c, dtype, splits: int, idx) -> np.ndarray:
+        A = np.ascontiguousarray(A, np.uint32)
+        B = np.ascontiguousarray(B, np.uint32)
+        C = None if C is None else np.ascontiguousarray(C, np.float32)
+        batch, M_rep, K_rep = A.shape[:3]
+        N_rep, ka = B.shape[1], 2 * A.shape[4]
+        idx = np.ascontiguousarray(idx, np.int64).reshape(-1, 3)
+        out = np.empty(len(idx), np.float32)
+        rc = self.L.oracle_mma_splitk_sampled(_ptr(out), _ptr(idx), len(idx), _ptr(A), _ptr(B),
+                                              _ptr(C), float(c), batch, M_rep, N_rep, K_rep, ka,
+                                              splits, _DTYPES[dtype])
+        if rc != 0:
+            raise ValueError("oracle_mma_splitk_sampled rejected its arguments")
+        return out
+
+
 def _ptr(a: np.ndarray | None):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
@@ -317,6 +389,20 @@ def bound(A, B, C, c, dtype, idx=None):
 
 def box_copy(src, box, coords, n_repeat=1, coord_step=None, dims=None, strides=None):
     return default().box_copy(src, box, coords, n_repeat, coord_step, dims, strides)
+
+
+def box_store(G, img, box, coords, n_repeat=1, coord_step=None, op="store", elem_type=None,
+              dims=None, strides=None):
+    return default().box_store(G, img, box, coords, n_repeat, coord_step, op, elem_type, dims,
+                               strides)
+
+
+def mma_splitk(A, B, C, c, dtype, splits):
+    return default().mma_splitk(A, B, C, c, dtype, splits)
+
+
+def mma_splitk_sampled(A, B, C, c, dtype, splits, idx):
+    return default().mma_splitk_sampled(A, B, C, c, dtype, splits, idx)
 
 
 def build_variant(source_text: str, out_path: str) -> str:

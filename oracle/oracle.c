@@ -22,6 +22,12 @@
  *   - cp.async.bulk.tensor page, "Operands and descriptor fields" and
  *     "Example: two explicit 8x16 boxes": box / coords / coord_steps, the
  *     compact (repeat, box...) image, out-of-bounds fill defaulting to zero.
+ *   - cp.async.bulk.tensor page, "Stores, reductions, and completion": the
+ *     store and the add reduction take the same box contract with the global
+ *     tensor as destination; a reduction destination holds its starting
+ *     value before the first reduction (the split-K form's C).
+ *   - mma.sync page introduction and shapes table: the m16n8k8 form (k = 8
+ *     atoms, k/2 = 4 words per atom row).
  *
  * Readings where the pages leave a step open:
  *   - within one hardware issue the summation order is not stated; the oracle
@@ -38,7 +44,10 @@
  * numpy/torch half decoders for h2f; int64 exact arithmetic for quarter-
  * integer inputs (the page's worked example is one); float64 numpy matmul
  * within the fp32 error bound for normal inputs; the page's two-box example
- * for the box copy; brute-force padding for out-of-bounds boxes.
+ * for the box copy and store; brute-force padding for out-of-bounds boxes;
+ * numpy float32/float16, torch bfloat16 and wrap-around integer additions for
+ * the add reduction; single-rounding cases that fix the split-K boundaries
+ * and the order in which partial sums meet C.
  */
 #include <math.h>
 #include <stdint.h>
@@ -251,6 +260,70 @@ int oracle_mma_scaled(float* D, const uint32_t* A, const uint32_t* B, const floa
   return 0;
 }
 
+/* Split-K form: the K axis is cut at multiples of 32 values into S_eff =
+ * min(splits, n) contiguous ranges of whole 32-value steps (n = ceil(K/32));
+ * split s takes steps [s*n/S_eff, (s+1)*n/S_eff) (integer division), so every
+ * range is non-empty. Each range is summed from zero, k ascending. The result
+ * starts at C and the partial sums are added to it one at a time, s
+ * ascending: the add reduction of the cp.async.bulk.tensor page ("Stores,
+ * reductions, and completion"), whose destination holds the intended starting
+ * value before the first reduction. K = 0 leaves D = C. */
+static float one_output_splitk(const uint32_t* A, const uint32_t* B, const float* C, float c,
+                               int64_t b, int64_t m, int64_t n, int64_t M_rep, int64_t N_rep,
+                               int64_t K_rep, int64_t ka, int64_t splits, int dtype) {
+  const int64_t K = ka * K_rep, steps = (K + 31) / 32;
+  const int64_t S = splits < steps ? splits : steps;
+  float d = C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c;
+  for (int64_t s = 0; s < S; ++s) {
+    const int64_t lo = 32 * (s * steps / S);
+    int64_t hi = 32 * ((s + 1) * steps / S);
+    if (hi > K) hi = K;
+    float part = 0.0f;
+    for (int64_t k = lo; k < hi; ++k) {
+      float a = packed_elem(A, b, m, k, 16, M_rep, K_rep, ka, dtype);
+      float x = packed_elem(B, b, n, k, 8, N_rep, K_rep, ka, dtype);
+      part = part + a * x;
+    }
+    d = d + part;
+  }
+  return d;
+}
+
+int oracle_mma_splitk(float* D, const uint32_t* A, const uint32_t* B, const float* C, float c,
+                      int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep, int64_t ka,
+                      int64_t splits, int dtype) {
+  if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+  if ((ka != 16 && ka != 8) || splits < 1) return -1;
+  const int64_t rows = batch * 16 * M_rep;
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t bm = 0; bm < rows; ++bm) {
+    const int64_t b = bm / (16 * M_rep), m = bm % (16 * M_rep);
+    for (int64_t n = 0; n < 8 * N_rep; ++n)
+      D[acc_offset(b, m, n, M_rep, N_rep)] =
+          one_output_splitk(A, B, C, c, b, m, n, M_rep, N_rep, K_rep, ka, splits, dtype);
+  }
+  return 0;
+}
+
+int oracle_mma_splitk_sampled(float* out, const int64_t* idx, int64_t count, const uint32_t* A,
+                              const uint32_t* B, const float* C, float c, int64_t batch,
+                              int64_t M_rep, int64_t N_rep, int64_t K_rep, int64_t ka,
+                              int64_t splits, int dtype) {
+  if (dtype != ORACLE_F16 && dtype != ORACLE_BF16) return -1;
+  if ((ka != 16 && ka != 8) || splits < 1) return -1;
+  for (int64_t i = 0; i < count; ++i) {
+    const int64_t *t = idx + 3 * i;
+    if (t[0] < 0 || t[0] >= batch || t[1] < 0 || t[1] >= 16 * M_rep || t[2] < 0 ||
+        t[2] >= 8 * N_rep)
+      return -1;
+  }
+#pragma omp parallel for schedule(dynamic)
+  for (int64_t i = 0; i < count; ++i)
+    out[i] = one_output_splitk(A, B, C, c, idx[3 * i], idx[3 * i + 1], idx[3 * i + 2], M_rep,
+                               N_rep, K_rep, ka, splits, dtype);
+  return 0;
+}
+
 /* Selected outputs only: idx holds count triples (b, m, n); out[i] gets D[b, m, n]. */
 int oracle_mma_sampled_k(float* out, const int64_t* idx, int64_t count, const uint32_t* A,
                          const uint32_t* B, const float* C, float c, int64_t batch,
@@ -314,6 +387,128 @@ int64_t oracle_box_copy(uint8_t* img, const uint8_t* G, int32_t rank, int32_t el
         memcpy(out, G + off, (size_t)elem_bytes);
       else
         memset(out, 0, (size_t)elem_bytes);
+    }
+  }
+  return (int64_t)n_repeat * box_elems * elem_bytes;
+}
+
+/* ---- box store and add reduction (compact image -> global tensor region) ----
+ * cp.async.bulk.tensor page, "Stores, reductions, and completion": the load's
+ * coordinate/box contract with the global tensor as destination. For each
+ * repeat t (ascending) and box element j (innermost fastest) whose global
+ * coordinate coords + t*coord_step + j lies inside dims in every dimension:
+ *   op 0 (store):  G[...] = img[t, j]
+ *   op 1 (add):    G[...] = G[...] + img[t, j], one rounding per add in the
+ *                  element type (1 f32, 2 f16, 3 bf16, 4 i32, 5 i64; integer
+ *                  adds wrap modulo 2^32 / 2^64).
+ * Elements outside dims are not written. Returns the image bytes consumed
+ * (n_repeat * prod(box) * elem_bytes) or -1.
+ */
+
+/* x rounded to the nearest value with p significand bits, exponents in
+ * [emin, emax] (gradual underflow below 2^emin), ties to even; beyond the
+ * largest finite value it becomes infinity (IEEE-754 round to nearest). */
+static double round_to_format(double x, int p, int emin, int emax) {
+  if (x == 0.0 || !isfinite(x)) return x;
+  int e;
+  frexp(x, &e); /* |x| in [2^(e-1), 2^e) */
+  int lead = e - 1;
+  if (lead < emin) lead = emin;
+  const double q = ldexp(1.0, lead - (p - 1)); /* spacing of representable values near x */
+  const double r = nearbyint(x / q) * q;       /* default rounding mode: ties to even */
+  const double max_finite = ldexp(2.0 - ldexp(1.0, 1 - p), emax);
+  if (fabs(r) > max_finite) return copysign(INFINITY, x);
+  return r;
+}
+
+/* IEEE binary16 encoding of a value that binary16 represents exactly. */
+static uint16_t f16_encode(double r) {
+  if (isnan(r)) return 0x7e00u;
+  const uint16_t sign = signbit(r) ? 0x8000u : 0u;
+  const double a = fabs(r);
+  if (isinf(a)) return (uint16_t)(sign | 0x7c00u);
+  if (a < ldexp(1.0, -14)) return (uint16_t)(sign | (uint16_t)(a / ldexp(1.0, -24)));
+  int e;
+  const double f = frexp(a, &e); /* a = f * 2^e, f in [0.5, 1) */
+  return (uint16_t)(sign | (uint16_t)((e - 1 + 15) << 10) | (uint16_t)((2.0 * f - 1.0) * 1024.0));
+}
+
+/* bfloat16 encoding (top half of binary32) of a value bfloat16 represents exactly. */
+static uint16_t bf16_encode(double r) {
+  if (isnan(r)) return 0x7fc0u;
+  const float f = (float)r;
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  return (uint16_t)(u >> 16);
+}
+
+static void add_into(uint8_t* g, const uint8_t* v, int elem_type) {
+  if (elem_type == 1) {
+    float x, y;
+    memcpy(&x, g, 4);
+    memcpy(&y, v, 4);
+    const float z = x + y;
+    memcpy(g, &z, 4);
+  } else if (elem_type == 2 || elem_type == 3) {
+    uint16_t x, y;
+    memcpy(&x, g, 2);
+    memcpy(&y, v, 2);
+    const int dt = elem_type == 2 ? ORACLE_F16 : ORACLE_BF16;
+    const double sum = (double)oracle_h2f(x, dt) + (double)oracle_h2f(y, dt);
+    const uint16_t z = elem_type == 2 ? f16_encode(round_to_format(sum, 11, -14, 15))
+                                      : bf16_encode(round_to_format(sum, 8, -126, 127));
+    memcpy(g, &z, 2);
+  } else if (elem_type == 4) {
+    uint32_t x, y;
+    memcpy(&x, g, 4);
+    memcpy(&y, v, 4);
+    const uint32_t z = x + y;
+    memcpy(g, &z, 4);
+  } else {
+    uint64_t x, y;
+    memcpy(&x, g, 8);
+    memcpy(&y, v, 8);
+    const uint64_t z = x + y;
+    memcpy(g, &z, 8);
+  }
+}
+
+int64_t oracle_box_store(uint8_t* G, const uint8_t* img, int32_t rank, int32_t elem_bytes,
+                         const int64_t* dims, const int64_t* strides, const int32_t* box,
+                         const int64_t* coords, int32_t n_repeat, const int64_t* coord_step,
+                         int32_t op, int32_t elem_type) {
+  if (rank < 1 || rank > 5 || n_repeat < 1 || (op != 0 && op != 1)) return -1;
+  if (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4 && elem_bytes != 8) return -1;
+  if (op == 1) {
+    static const int type_bytes[6] = {0, 4, 2, 2, 4, 8};
+    if (elem_type < 1 || elem_type > 5 || type_bytes[elem_type] != elem_bytes) return -1;
+  }
+  int64_t box_elems = 1;
+  for (int d = 0; d < rank; ++d) {
+    if (box[d] < 1 || box[d] > 256 || dims[d] < 1) return -1;
+    box_elems *= box[d];
+  }
+  if (strides[rank - 1] != elem_bytes) return -1;
+  for (int32_t t = 0; t < n_repeat; ++t) {
+    for (int64_t e = 0; e < box_elems; ++e) {
+      int64_t j[5], rem = e;
+      for (int d = rank - 1; d >= 0; --d) {
+        j[d] = rem % box[d];
+        rem /= box[d];
+      }
+      int inside = 1;
+      int64_t off = 0;
+      for (int d = 0; d < rank; ++d) {
+        const int64_t g = coords[d] + coord_step[d] * (int64_t)t + j[d];
+        if (g < 0 || g >= dims[d]) inside = 0;
+        off += g * strides[d];
+      }
+      if (!inside) continue;
+      const uint8_t* in = img + (e + (int64_t)t * box_elems) * elem_bytes;
+      if (op == 0)
+        memcpy(G + off, in, (size_t)elem_bytes);
+      else
+        add_into(G + off, in, elem_type);
     }
   }
   return (int64_t)n_repeat * box_elems * elem_bytes;

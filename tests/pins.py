@@ -329,4 +329,215 @@ def pin_box_oob(o):
         assert nbytes == rep * int(np.prod(box)) * np.dtype(dtype).itemsize
 
 
+# ---- box store and add reduction (cp.async.bulk.tensor page, "Stores,
+# reductions, and completion") ----
+
+def _padded_store(G, img, box, coords, step, combine):
+    """Brute force: pad G, apply each repeat's image to its slice with numpy
+    in repeat order, crop."""
+    pad = 300
+    xp = np.pad(G, [(pad, pad)] * G.ndim)
+    inside = np.pad(np.ones(G.shape, bool), [(pad, pad)] * G.ndim)
+    for t in range(img.shape[0]):
+        sl = tuple(slice(pad + c + t * st, pad + c + t * st + bx)
+                   for c, st, bx in zip(coords, step, box))
+        m = inside[sl]
+        xp[sl] = np.where(m, combine(xp[sl], img[t]), xp[sl])
+    return xp[tuple(slice(pad, pad + n) for n in G.shape)]
+
+
+def pin_box_store_page_example(o):
+    """The page's two-box example read backwards: storing the (2, 8, 16) image
+    of arange(256) at (0, 0) with step (8, 0) rebuilds the 16x16 tensor, and a
+    store after a load of the same boxes is the identity."""
+    x = np.arange(256, dtype=np.uint32).reshape(16, 16)
+    out, nbytes = o.box_store(np.zeros_like(x), x.reshape(2, 8, 16), (8, 16), (0, 0), 2, (8, 0))
+    assert np.array_equal(out, x) and nbytes == 1024
+    rng = np.random.default_rng(12)
+    y = rng.integers(0, 1 << 16, (12, 40)).astype(np.uint16)
+    img, _ = o.box_copy(y, (4, 16), (2, 8), 3, (3, 1))
+    back, _ = o.box_store(np.zeros_like(y), img, (4, 16), (2, 8), 3, (3, 1))
+    touched = np.zeros(y.shape, bool)
+    for t in range(3):
+        touched[2 + 3 * t: 6 + 3 * t, 8 + t: 24 + t] = True
+    assert np.array_equal(back[touched], y[touched]) and not back[~touched].any()
+
+
+def pin_box_store_oob(o):
+    """Stores partly outside the tensor write only the inside elements, and
+    overlapping repeats leave the last repeat's values; checked against numpy
+    slice assignment on a padded copy, for ranks 1-3 and several element sizes."""
+    rng = np.random.default_rng(13)
+    cases = [
+        (np.uint32, (16, 16), (8, 16), (-3, 5), 3, (6, -4)),
+        (np.uint16, (5, 7, 9), (4, 4, 8), (3, -2, 4), 2, (-4, 3, 1)),
+        (np.uint8, (37,), (32,), (20,), 2, (-25,)),
+        (np.uint64, (9, 11), (3, 5), (0, 0), 4, (1, 2)),      # repeats overlap
+        (np.uint32, (8, 8), (4, 4), (2, 2), 3, (0, 0)),        # same box three times
+    ]
+    for dtype, shape, box, coords, rep, step in cases:
+        G = rng.integers(1, 200, shape).astype(dtype)
+        img = rng.integers(1, 200, (rep, *box)).astype(dtype)
+        got, nbytes = o.box_store(G, img, box, coords, rep, step)
+        ref = _padded_store(G, img, box, coords, step, lambda old, new: new)
+        assert np.array_equal(got, ref), (dtype, shape)
+        assert nbytes == rep * int(np.prod(box)) * np.dtype(dtype).itemsize
+
+
+def _finite_bits(rng, shape, dt):
+    bits = rng.integers(0, 1 << 16, shape, dtype=np.uint32).astype(np.uint16)
+    expo_all_ones = 0x7C00 if dt == "f16" else 0x7F80
+    return np.where((bits & expo_all_ones) == expo_all_ones, bits & ~np.uint16(0x4000), bits)
+
+
+def pin_box_reduce_library_adds(o):
+    """The add reduction of one element is the library's own addition in the
+    element type: numpy float32 / float16 (computed through float32 and rounded
+    once more, which is exact rounding for these formats), torch bfloat16 on
+    the CPU, and wrap-around int32 / int64. Operands are random finite bit
+    patterns, so ties, subnormals and overflow to infinity all occur."""
+    import torch
+    rng = np.random.default_rng(14)
+    shape, box, coords = (24, 40), (16, 32), (3, 5)
+    sl = (slice(3, 19), slice(5, 37))
+    G32 = rng.standard_normal(shape).astype(np.float32) * np.float32(1e3)
+    I32 = rng.standard_normal((1, *box)).astype(np.float32)
+    got, _ = o.box_store(G32, I32, box, coords, op="add", elem_type="f32")
+    ref = G32.copy()
+    ref[sl] = ref[sl] + I32[0]
+    assert np.array_equal(got, ref)
+    for dt in ("f16", "bf16"):
+        G = _finite_bits(rng, shape, dt)
+        img = _finite_bits(rng, (1, *box), dt)
+        got, _ = o.box_store(G, img, box, coords, op="add", elem_type=dt)
+        ref = G.copy()
+        if dt == "f16":
+            with np.errstate(over="ignore"):
+                ref[sl] = (G[sl].view(np.float16) + img[0].view(np.float16)).view(np.uint16)
+        else:
+            tg = torch.from_numpy(G[sl].view(np.int16).copy()).view(torch.bfloat16)
+            ti = torch.from_numpy(img[0].view(np.int16).copy()).view(torch.bfloat16)
+            ref[sl] = (tg + ti).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(got, ref), dt
+    for it, dt in ((np.int32, "i32"), (np.int64, "i64")):
+        info = np.iinfo(it)
+        G = rng.integers(info.min, info.max, shape, dtype=it)
+        img = rng.integers(info.min, info.max, (1, *box), dtype=it)
+        got, _ = o.box_store(G, img, box, coords, op="add", elem_type=dt)
+        ref = G.copy()
+        with np.errstate(over="ignore"):
+            ref[sl] = G[sl] + img[0]
+        assert np.array_equal(got, ref), dt
+
+
+def pin_box_reduce_order(o):
+    """Overlapping repeats are added one at a time in repeat order, each add
+    rounded: 1 + 2^-24 + 2^-24 stays 1 (ties to even twice), where summing
+    the images first would give 1 + 2^-23. Partly outside boxes add only
+    inside elements; checked against numpy on a padded copy."""
+    one = np.ones((4, 4), np.float32)
+    img = np.full((2, 4, 4), 2.0 ** -24, np.float32)
+    got, _ = o.box_store(one, img, (4, 4), (0, 0), 2, (0, 0), op="add", elem_type="f32")
+    assert (got == 1.0).all()
+    rng = np.random.default_rng(15)
+    G = rng.standard_normal((9, 11)).astype(np.float32)
+    img = rng.standard_normal((4, 3, 5)).astype(np.float32)
+    got, _ = o.box_store(G, img, (3, 5), (-1, 7), 4, (2, -1), op="add", elem_type="f32")
+    ref = _padded_store(G, img, (3, 5), (-1, 7), (2, -1), lambda old, new: old + new)
+    assert np.array_equal(got, ref)
+
+
+# ---- split-K form ----
+
+def _splitk_bounds(K, S):
+    steps = -(-K // 32)
+    S = min(S, steps)
+    return [(32 * (s * steps // S), min(32 * ((s + 1) * steps // S), K)) for s in range(S)]
+
+
+def pin_splitk_exact_and_degenerate(o):
+    """Quarter-integer data: every split count gives the same bits as the
+    recurrence (all sums exact). One split with C = 0 is the recurrence itself
+    on normal data. K = 0 leaves D = C bit for bit, -0 included."""
+    rng = np.random.default_rng(16)
+    for dt, (M, N, K) in (("bf16", (32, 24, 224)), ("f16", (16, 40, 96))):
+        a = _quarter_bits(rng, (2, M, K), dt)
+        b = _quarter_bits(rng, (2, N, K), dt)
+        A, B = o.pack(a, 16), o.pack(b, 8)
+        C = (rng.integers(-64, 65, (2, M // 16, N // 8, 16, 8)) / 4).astype(np.float32)
+        ref = o.mma(A, B, C, 0.0, dt)
+        for S in (1, 2, 3, 5, 7, 100):
+            assert np.array_equal(o.mma_splitk(A, B, C, 0.0, dt, S), ref), (dt, S)
+    a = workloads.f32_to_bf16_bits(rng.standard_normal((1, 32, 160)).astype(np.float32))
+    b = workloads.f32_to_bf16_bits(rng.standard_normal((1, 16, 160)).astype(np.float32))
+    A, B = o.pack(a, 16), o.pack(b, 8)
+    assert np.array_equal(o.mma_splitk(A, B, None, 0.0, "bf16", 1), o.mma(A, B, None, 0.0, "bf16"))
+    C = rng.standard_normal((1, 2, 2, 16, 8)).astype(np.float32)
+    C[0, 0, 0, 0, :4] = -0.0
+    A0 = np.zeros((1, 2, 0, 16, 8), np.uint32)
+    B0 = np.zeros((1, 2, 0, 8, 8), np.uint32)
+    D0 = o.mma_splitk(A0, B0, C, 0.0, "bf16", 4)
+    assert np.array_equal(D0.view(np.uint32), C.view(np.uint32))
+
+
+def pin_splitk_boundaries_and_order(o):
+    """Where the K axis is cut and how the partial sums meet C, fixed by
+    single-rounding cases. K = 160 is 5 steps of 32; two splits take steps
+    [0, 2) and [2, 5). C = 1, each product 2^-12 * 2^-12 = 2^-24:
+      column 0: products at k = 0, 1 (one split): 1 + 2^-23
+      column 1: products at k = 40, 70 (steps 1 and 2, two splits): 1
+      column 2: products at k = 100, 130 (steps 3, 4, one split): 1 + 2^-23
+    With a single split every column is 1 + 2^-23 (C meets the whole partial
+    sum once), while the C-first recurrence gives 1 everywhere."""
+    K = 160
+    assert _splitk_bounds(K, 2) == [(0, 64), (64, 160)]
+    h = np.float32(2.0 ** -12)
+    a = np.zeros((1, 16, K), np.float32)
+    b = np.zeros((1, 8, K), np.float32)
+    a[0, 0, [0, 1, 40, 70, 100, 130]] = h
+    b[0, 0, [0, 1]] = h
+    b[0, 1, [40, 70]] = h
+    b[0, 2, [100, 130]] = h
+    b[0, 3, [40, 70]] = h
+    A = o.pack(workloads.f32_to_bf16_bits(a), 16)
+    B = o.pack(workloads.f32_to_bf16_bits(b), 8)
+    big = np.float32(1 + 2.0 ** -23)
+    D2 = o.mma_splitk(A, B, None, 1.0, "bf16", 2)[0, 0, 0, 0, :4]
+    assert list(D2[:3]) == [big, 1.0, big], D2
+    D1 = o.mma_splitk(A, B, None, 1.0, "bf16", 1)[0, 0, 0, 0, :4]
+    assert (D1 == big).all(), D1
+    assert (o.mma(A, B, None, 1.0, "bf16")[0, 0, 0, 0, :4] == 1.0).all()
+
+
+def pin_splitk_normal_and_layouts(o):
+    """Normal bf16 data, C tensor: every split count stays within
+    gamma_(K+S+1) (|A||B|^T + |C|) of the float64 product (at most K + S + 1
+    roundings on any path); the k = 8 layout of the same operands gives the
+    same bits; sampled outputs equal the full result."""
+    rng = np.random.default_rng(17)
+    M, N, K = 32, 24, 328
+    a = workloads.f32_to_bf16_bits(rng.standard_normal((1, M, K)).astype(np.float32))
+    b = workloads.f32_to_bf16_bits(rng.standard_normal((1, N, K)).astype(np.float32))
+    C = rng.standard_normal((1, M // 16, N // 8, 16, 8)).astype(np.float32)
+    Kp = K + (-K) % 16
+    a16 = np.pad(a, ((0, 0), (0, 0), (0, Kp - K)))
+    b16 = np.pad(b, ((0, 0), (0, 0), (0, Kp - K)))
+    A16, B16 = o.pack(a16, 16), o.pack(b16, 8)
+    A8, B8 = o.pack_k8(a, 16), o.pack_k8(b, 8)
+    af, bf = util.decode(a[0], "bf16"), util.decode(b[0], "bf16")
+    exact = af @ bf.T + util.tile_to_logical(C)[0].astype(np.float64)
+    mag = np.abs(af) @ np.abs(bf).T + np.abs(util.tile_to_logical(C)[0])
+    for S in (1, 2, 3, 11):
+        D8 = o.mma_splitk(A8, B8, C, 0.0, "bf16", S)
+        err = np.abs(util.tile_to_logical(D8)[0] - exact)
+        assert (err <= util.gamma(K + S + 1) * mag).all(), S
+        # k = 16 holds the same values plus zero padding: same bits where the
+        # padding does not move a split boundary
+        if _splitk_bounds(K, S) == [(lo, min(hi, K)) for lo, hi in _splitk_bounds(Kp, S)]:
+            assert np.array_equal(o.mma_splitk(A16, B16, C, 0.0, "bf16", S), D8), S
+        idx = util.sample_indices(rng, 1, M, N, 40)
+        got = o.mma_splitk_sampled(A8, B8, C, 0.0, "bf16", S, idx)
+        assert np.array_equal(got, util.tile_to_logical(D8)[idx[:, 0], idx[:, 1], idx[:, 2]])
+
+
 ALL_PINS = {name: fn for name, fn in globals().items() if name.startswith("pin_")}

@@ -70,6 +70,41 @@ MUTATIONS = {
         "img + ((int64_t)t * box_elems + e) * elem_bytes",
         "img + (e * n_repeat + t) * elem_bytes",
         ["pin_box_page_example", "pin_box_oob"]),
+    "store_writes_outside": (
+        "      if (!inside) continue;\n      const uint8_t* in",
+        "      if (!inside) off = 0;\n      const uint8_t* in",
+        ["pin_box_store_oob", "pin_box_reduce_order"]),
+    "store_repeats_reversed": (
+        "const int64_t g = coords[d] + coord_step[d] * (int64_t)t + j[d];",
+        "const int64_t g = coords[d] + coord_step[d] * (int64_t)(n_repeat - 1 - t) + j[d];",
+        ["pin_box_store_oob", "pin_box_reduce_order"]),
+    "reduce_f16_truncates": (
+        "const double q = ldexp(1.0, lead - (p - 1)); /* spacing of representable values near x */\n"
+        "  const double r = nearbyint(x / q) * q;",
+        "const double q = ldexp(1.0, lead - (p - 1)); /* spacing of representable values near x */\n"
+        "  const double r = trunc(x / q) * q;",
+        ["pin_box_reduce_library_adds"]),
+    "reduce_no_overflow_to_inf": (
+        "if (fabs(r) > max_finite) return copysign(INFINITY, x);",
+        "if (fabs(r) > max_finite) return copysign(max_finite, x);",
+        ["pin_box_reduce_library_adds"]),
+    "splitk_boundary_rounded_up": (
+        "int64_t hi = 32 * ((s + 1) * steps / S);",
+        "int64_t hi = 32 * (((s + 1) * steps + S - 1) / S);",
+        ["pin_splitk_boundaries_and_order"]),
+    "splitk_partials_summed_before_c": (
+        '  float d = C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c;\n  for (int64_t s = 0; s < S; ++s) {\n    const int64_t lo = 32 * (s * steps / S);\n    int64_t hi = 32 * ((s + 1) * steps / S);\n    if (hi > K) hi = K;\n    float part = 0.0f;\n    for (int64_t k = lo; k < hi; ++k) {\n      float a = packed_elem(A, b, m, k, 16, M_rep, K_rep, ka, dtype);\n      float x = packed_elem(B, b, n, k, 8, N_rep, K_rep, ka, dtype);\n      part = part + a * x;\n    }\n    d = d + part;\n  }\n  return d;',
+        '  float d = 0.0f;\n  for (int64_t s = 0; s < S; ++s) {\n    const int64_t lo = 32 * (s * steps / S);\n    int64_t hi = 32 * ((s + 1) * steps / S);\n    if (hi > K) hi = K;\n    float part = 0.0f;\n    for (int64_t k = lo; k < hi; ++k) {\n      float a = packed_elem(A, b, m, k, 16, M_rep, K_rep, ka, dtype);\n      float x = packed_elem(B, b, n, k, 8, N_rep, K_rep, ka, dtype);\n      part = part + a * x;\n    }\n    d = d + part;\n  }\n  return S ? d + (C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c) : (C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c);',
+        ["pin_splitk_boundaries_and_order"]),
+    "splitk_c_ignored": (
+        "  float d = C ? C[acc_offset(b, m, n, M_rep, N_rep)] : c;\n  for (int64_t s = 0;",
+        "  float d = 0.0f;\n  for (int64_t s = 0;",
+        ["pin_splitk_exact_and_degenerate", "pin_splitk_boundaries_and_order",
+         "pin_splitk_normal_and_layouts"]),
+    "splitk_last_range_dropped": (
+        "  for (int64_t s = 0; s < S; ++s) {\n    const int64_t lo",
+        "  for (int64_t s = 0; s + 1 < S; ++s) {\n    const int64_t lo",
+        ["pin_splitk_exact_and_degenerate", "pin_splitk_normal_and_layouts"]),
 }
 
 
