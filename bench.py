@@ -105,7 +105,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=workloads.HEADLINE, choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--workload", default=workloads.HEADLINE,
+                    choices=sorted(workloads.WORKLOADS) + sorted(workloads.EXTRA_WORKLOADS))
     ap.add_argument("--kernel", default="auto", choices=["auto", "direct", "tiled", "skinny"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -118,6 +119,8 @@ def main():
     ap.add_argument("--atom-k", type=int, default=16, choices=[16, 8],
                     help="K depth of a packed atom: 16, or 8 for the m16n8k8 layout "
                          "(pack_operand_k8 + mma_tile_opts)")
+    ap.add_argument("--splitk", type=int, default=None,
+                    help="run the split-K form with this many splits (0: the library's default)")
     args = ap.parse_args()
     if args.kmajor and args.atom_k != 16:
         ap.error("--kmajor packs the k = 16 layout only")
@@ -136,7 +139,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = workloads.WORKLOADS[args.workload]
+    w = {**workloads.WORKLOADS, **workloads.EXTRA_WORKLOADS}[args.workload]
     log(f"[bench] workload {w.name}: batch={w.batch} M={w.M} N={w.N} K={w.K} {w.dtype} "
         f"C={'tensor' if w.c_tensor else 'scalar'}")
     inp = workloads.make_inputs(w, seed=0)
@@ -155,6 +158,14 @@ def main():
     D = torch.empty((w.batch, w.M_rep, w.N_rep, 16, 8), dtype=torch.float32, device=dev)
     kernel = bmm.select_kernel(w.batch, w.M_rep, w.N_rep, w.K_rep) if args.kernel == "auto" \
         else args.kernel
+    splits, WS = None, None
+    if args.splitk is not None:
+        if args.alpha is not None or args.beta is not None:
+            ap.error("--splitk computes the plain form only")
+        splits = args.splitk or bmm.splitk_default(w.batch, w.M_rep, w.N_rep, w.K // ka, ka)
+        ws_bytes = bmm.splitk_workspace_bytes(w.batch, w.M_rep, w.N_rep, w.K // ka, ka, splits)
+        WS = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev)
+        kernel = f"tiled+splitk{splits}"
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -166,7 +177,11 @@ def main():
         pack(b, 8, out=B, **pack_kw)
         if ev is not None:
             ev[2].record(stream)
-        bmm.mma_tile(A, B, C, c, w.dtype, out=D, kernel=kernel, alpha=args.alpha, beta=args.beta)
+        if splits is not None:
+            bmm.mma_tile_splitk(A, B, C, c, w.dtype, splits, out=D, workspace=WS)
+        else:
+            bmm.mma_tile(A, B, C, c, w.dtype, out=D, kernel=kernel, alpha=args.alpha,
+                         beta=args.beta)
         if ev is not None:
             ev[3].record(stream)
 
@@ -226,7 +241,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
                    "c": "tensor" if w.c_tensor else "scalar", "kernel": kernel,
-                   "alpha": args.alpha, "beta": args.beta, "atom_k": ka,
+                   "alpha": args.alpha, "beta": args.beta, "atom_k": ka, "splitk": splits,
                    "step": ("pack_kmajor A + pack_kmajor B + mma_tile" if args.kmajor
                             else "pack A + pack B + mma_tile")},
         "roofline": roofline,

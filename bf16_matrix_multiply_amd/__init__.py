@@ -23,8 +23,10 @@ import os
 
 import torch
 
-__all__ = ["BmmError", "pack_operand", "pack_operand_kmajor", "box_copy", "mma_tile", "select_kernel",
-           "library_path", "KERNELS", "MmaOpts"]
+__all__ = ["BmmError", "pack_operand", "pack_operand_kmajor", "box_copy", "box_store",
+           "box_reduce_add", "mma_tile", "mma_tile_splitk", "splitk_default",
+           "splitk_workspace_bytes", "select_kernel", "library_path", "KERNELS", "MmaOpts",
+           "ELEM_TYPES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libbmm.so")
@@ -33,6 +35,7 @@ BMM_F16, BMM_BF16 = 0, 1
 _DTYPES = {"f16": BMM_F16, "float16": BMM_F16, torch.float16: BMM_F16,
            "bf16": BMM_BF16, "bfloat16": BMM_BF16, torch.bfloat16: BMM_BF16}
 KERNELS = {"auto": 0, "direct": 1, "tiled": 2, "skinny": 3}
+ELEM_TYPES = {"f32": 1, "f16": 2, "bf16": 3, "i32": 4, "i64": 5}
 KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
 
 
@@ -99,9 +102,18 @@ def lib():
         L.bmm_mma_tile_scaled.argtypes = [p, p, p, p, ctypes.c_float, ctypes.c_float,
                                           ctypes.c_float, i64, i64, i64, i64, ctypes.c_int, i32, p]
         L.bmm_select_kernel.argtypes = [i64, i64, i64, i64]
+        L.bmm_box_store.argtypes = [p, p, ctypes.POINTER(BoxDesc), ctypes.POINTER(i64), p]
+        L.bmm_box_reduce_add.argtypes = [p, p, ctypes.POINTER(BoxDesc), i32,
+                                         ctypes.POINTER(i64), p]
+        L.bmm_mma_tile_splitk.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64, i64,
+                                          ctypes.c_int, i32, i32, p, i64, p]
+        L.bmm_mma_splitk_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
+        L.bmm_mma_splitk_workspace_bytes.restype = i64
+        L.bmm_splitk_default.argtypes = [i64, i64, i64, i64, i32]
         for f in (L.bmm_pack_operand, L.bmm_pack_operand_kmajor, L.bmm_pack_operand_k8,
                   L.bmm_box_copy, L.bmm_mma_tile, L.bmm_mma_tile_with, L.bmm_mma_tile_scaled,
-                  L.bmm_mma_tile_opts, L.bmm_select_kernel):
+                  L.bmm_mma_tile_opts, L.bmm_select_kernel, L.bmm_box_store,
+                  L.bmm_box_reduce_add, L.bmm_mma_tile_splitk, L.bmm_splitk_default):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -192,19 +204,7 @@ def box_copy(src: torch.Tensor, box, coords, n_repeat: int = 1, coord_step=None,
     dims/strides default to ``src``'s own extents and byte strides (outer to
     inner); strides are in bytes."""
     _require_cuda(src)
-    rank = len(box)
-    dims = list(src.shape) if dims is None else list(dims)
-    strides = [s * src.element_size() for s in src.stride()] if strides is None else list(strides)
-    coord_step = [0] * rank if coord_step is None else list(coord_step)
-    if not (len(dims) == len(strides) == len(coords) == len(coord_step) == rank):
-        raise ValueError("box_copy: box, coords, coord_step, dims and strides need one entry "
-                         "per dimension")
-    d = BoxDesc()
-    d.rank, d.elem_bytes = rank, src.element_size()
-    for i in range(rank):
-        d.dims[i], d.strides[i], d.box[i] = dims[i], strides[i], box[i]
-        d.coords[i], d.coord_step[i] = coords[i], coord_step[i]
-    d.n_repeat, d.swizzle, d.oob_fill = n_repeat, swizzle, oob_fill
+    d = _box_desc(src, box, coords, n_repeat, coord_step, swizzle, dims, strides, oob_fill)
     shape = (n_repeat, *box)
     if out is None:
         out = torch.empty(shape, dtype=src.dtype, device=src.device)
@@ -212,6 +212,105 @@ def box_copy(src: torch.Tensor, box, coords, n_repeat: int = 1, coord_step=None,
     _check(lib().bmm_box_copy(_ptr(out), _ptr(src), ctypes.byref(d), ctypes.byref(nbytes),
                               _stream(src)))
     return out, nbytes.value
+
+
+def _box_desc(t: torch.Tensor, box, coords, n_repeat, coord_step, swizzle, dims, strides,
+              oob_fill=0) -> BoxDesc:
+    rank = len(box)
+    dims = list(t.shape) if dims is None else list(dims)
+    strides = [s * t.element_size() for s in t.stride()] if strides is None else list(strides)
+    coord_step = [0] * rank if coord_step is None else list(coord_step)
+    if not (len(dims) == len(strides) == len(coords) == len(coord_step) == rank):
+        raise ValueError("box: box, coords, coord_step, dims and strides need one entry "
+                         "per dimension")
+    d = BoxDesc()
+    d.rank, d.elem_bytes = rank, t.element_size()
+    for i in range(rank):
+        d.dims[i], d.strides[i], d.box[i] = dims[i], strides[i], box[i]
+        d.coords[i], d.coord_step[i] = coords[i], coord_step[i]
+    d.n_repeat, d.swizzle, d.oob_fill = n_repeat, swizzle, oob_fill
+    return d
+
+
+def box_store(dst: torch.Tensor, image: torch.Tensor, box, coords, n_repeat: int = 1,
+              coord_step=None, swizzle: int = 0, dims=None, strides=None) -> int:
+    """Write the compact (n_repeat, *box) ``image`` into ``dst``'s boxes (in place;
+    elements outside the tensor are skipped). Returns the image bytes read."""
+    _require_cuda(dst, image)
+    if image.element_size() != dst.element_size() or not image.is_contiguous():
+        raise ValueError("box_store: image must be contiguous with dst's element size")
+    d = _box_desc(dst, box, coords, n_repeat, coord_step, swizzle, dims, strides)
+    nbytes = ctypes.c_int64(-1)
+    _check(lib().bmm_box_store(_ptr(dst), _ptr(image), ctypes.byref(d), ctypes.byref(nbytes),
+                               _stream(dst)))
+    return nbytes.value
+
+
+def box_reduce_add(dst: torch.Tensor, image: torch.Tensor, box, coords, elem_type: str,
+                   n_repeat: int = 1, coord_step=None, swizzle: int = 0, dims=None,
+                   strides=None) -> int:
+    """Add the compact (n_repeat, *box) ``image`` into ``dst``'s boxes (in place),
+    one rounding per add in ``elem_type`` ("f32", "f16", "bf16", "i32", "i64")."""
+    _require_cuda(dst, image)
+    if image.element_size() != dst.element_size() or not image.is_contiguous():
+        raise ValueError("box_reduce_add: image must be contiguous with dst's element size")
+    d = _box_desc(dst, box, coords, n_repeat, coord_step, swizzle, dims, strides)
+    nbytes = ctypes.c_int64(-1)
+    _check(lib().bmm_box_reduce_add(_ptr(dst), _ptr(image), ctypes.byref(d), ELEM_TYPES[elem_type],
+                                    ctypes.byref(nbytes), _stream(dst)))
+    return nbytes.value
+
+
+def splitk_workspace_bytes(batch, M_rep, N_rep, K_rep, atom_k, splits) -> int:
+    return _check(lib().bmm_mma_splitk_workspace_bytes(batch, M_rep, N_rep, K_rep, atom_k,
+                                                       splits))
+
+
+def splitk_default(batch, M_rep, N_rep, K_rep, atom_k=16) -> int:
+    return _check(lib().bmm_splitk_default(batch, M_rep, N_rep, K_rep, atom_k))
+
+
+def mma_tile_splitk(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None,
+                    c: float = 0.0, dtype="bf16", splits: int | None = None,
+                    out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Split-K form: D = (((C + P_0) + P_1) + ...), P_s the partial sums of
+    balanced ranges of 32-value K steps (bmm_mma_tile_splitk). ``splits``
+    defaults to bmm_splitk_default; ``workspace`` (float32, at least
+    bmm_mma_splitk_workspace_bytes) is allocated here when not given."""
+    _require_cuda(A, B, C, out, workspace)
+    if A.dim() != 5 or B.dim() != 5 or A.shape[3] != 16 or B.shape[3] != 8 or \
+            A.shape[4] not in (8, 4) or B.shape[4] != A.shape[4]:
+        raise ValueError("mma_tile_splitk: A must be (batch, M_rep, K_rep, 16, w) and B "
+                         "(batch, N_rep, K_rep, 8, w) packed words, w = 8 or 4")
+    atom_k = 2 * A.shape[4]
+    batch, M_rep, K_rep = A.shape[:3]
+    N_rep = B.shape[1]
+    if B.shape[0] != batch or B.shape[2] != K_rep:
+        raise ValueError("mma_tile_splitk: A and B disagree on batch or K_rep")
+    for t, name in ((A, "A"), (B, "B")):
+        if not t.is_contiguous() or t.element_size() != 4:
+            raise ValueError(f"mma_tile_splitk: {name} must be a contiguous 32-bit tensor")
+    shape = (batch, M_rep, N_rep, 16, 8)
+    if C is not None and (tuple(C.shape) != shape or C.dtype != torch.float32
+                          or not C.is_contiguous()):
+        raise ValueError(f"mma_tile_splitk: C must be a contiguous float32 tensor of shape {shape}")
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=A.device)
+    elif tuple(out.shape) != shape or out.dtype != torch.float32 or not out.is_contiguous():
+        raise ValueError(f"mma_tile_splitk: out must be a contiguous float32 tensor of shape {shape}")
+    if splits is None:
+        splits = splitk_default(batch, M_rep, N_rep, K_rep, atom_k)
+    need = splitk_workspace_bytes(batch, M_rep, N_rep, K_rep, atom_k, splits)
+    if workspace is None:
+        workspace = torch.empty(max(need // 4, 1), dtype=torch.float32, device=A.device)
+    elif not workspace.is_contiguous():
+        raise ValueError("mma_tile_splitk: workspace must be contiguous")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib().bmm_mma_tile_splitk(_ptr(out), _ptr(A), _ptr(B), _ptr(C), float(c), batch, M_rep,
+                                     N_rep, K_rep, _DTYPES[dtype], atom_k, splits,
+                                     _ptr(workspace), ws_bytes, _stream(A)))
+    return out
 
 
 def mma_tile(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None,

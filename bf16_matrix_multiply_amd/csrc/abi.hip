@@ -35,6 +35,28 @@ int choose_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K) {
   return BMM_KERNEL_DIRECT;
 }
 
+// Repeats t < u touch disjoint global boxes when some dimension steps by at
+// least the box extent (then every later repeat is further away still).
+bool repeats_disjoint(const bmm_box_desc& d) {
+  if (d.n_repeat == 1) return true;
+  for (int i = 0; i < d.rank; ++i) {
+    const int64_t st = d.coord_step[i] < 0 ? -d.coord_step[i] : d.coord_step[i];
+    if (st >= d.box[i]) return true;
+  }
+  return false;
+}
+
+int box_store_common(void* dst, const void* img, const bmm_box_desc& d, int elem_type,
+                     int64_t* bytes_moved, void* stream, const char* what) {
+  int64_t elems = 1;
+  for (int i = 0; i < d.rank; ++i) elems *= d.box[i];
+  const int rc = hip_status(bmm::launch_box_store(dst, img, d, elem_type, repeats_disjoint(d),
+                                                  static_cast<hipStream_t>(stream)),
+                            what);
+  if (rc == BMM_OK && bytes_moved) *bytes_moved = elems * d.elem_bytes * d.n_repeat;
+  return rc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -83,6 +105,26 @@ int bmm_box_copy(void* dst_image, const void* src, const bmm_box_desc* desc,
                             "box_copy launch");
   if (rc == BMM_OK && bytes_moved) *bytes_moved = elems * desc->elem_bytes * desc->n_repeat;
   return rc;
+}
+
+int bmm_box_store(void* dst, const void* src_image, const bmm_box_desc* desc,
+                  int64_t* bytes_moved, void* stream) {
+  bmm::Status st = bmm::check_box_store(dst, src_image, desc, 0, "box_store");
+  if (!st.ok()) return report(st);
+  return box_store_common(dst, src_image, *desc, 0, bytes_moved, stream, "box_store launch");
+}
+
+int bmm_box_reduce_add(void* dst, const void* src_image, const bmm_box_desc* desc,
+                       int32_t elem_type, int64_t* bytes_moved, void* stream) {
+  if (elem_type < BMM_ELEM_F32 || elem_type > BMM_ELEM_I64) {
+    g_last_error = "box_reduce_add: elem_type " + std::to_string(elem_type) +
+                   " is not a bmm_elem_type";
+    return BMM_EINVAL;
+  }
+  bmm::Status st = bmm::check_box_store(dst, src_image, desc, elem_type, "box_reduce_add");
+  if (!st.ok()) return report(st);
+  return box_store_common(dst, src_image, *desc, elem_type, bytes_moved, stream,
+                          "box_reduce_add launch");
 }
 
 int bmm_select_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep) {
@@ -141,6 +183,60 @@ int bmm_mma_tile_opts(float* D, const uint32_t* A, const uint32_t* B, const floa
   const bmm::MmaArgs a{D, A, B, C, c_scalar, batch, M_rep, N_rep, K_rep, int(dtype),
                        o.scaled, o.scaled ? o.alpha : 1.f, o.scaled ? o.beta : 1.f, o.atom_k};
   return mma_common(a, o.kernel, stream);
+}
+
+int64_t bmm_mma_splitk_workspace_bytes(int64_t batch, int64_t M_rep, int64_t N_rep,
+                                       int64_t K_rep, int32_t atom_k, int32_t splits) {
+  if (batch < 0 || M_rep < 0 || N_rep < 0 || K_rep < 0 || K_rep > (int64_t(1) << 26) ||
+      (atom_k != 16 && atom_k != 8) || splits < 1 || batch > (int64_t(1) << 40) ||
+      M_rep > (int64_t(1) << 40) || N_rep > (int64_t(1) << 40))
+    return BMM_EINVAL;
+  const __int128 bytes = __int128(bmm::splitk_effective(K_rep, atom_k, splits)) * batch * M_rep *
+                         N_rep * 512;
+  if (bytes > (__int128(1) << 50)) return BMM_EINVAL;
+  return int64_t(bytes);
+}
+
+int bmm_splitk_default(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep,
+                       int32_t atom_k) {
+  if (batch < 0 || M_rep < 0 || N_rep < 0 || K_rep < 0 || K_rep > (int64_t(1) << 26) ||
+      (atom_k != 16 && atom_k != 8))
+    return BMM_EINVAL;
+  // Enough 256 x 256 tiles x splits to give every CU a workgroup, with each
+  // split at least 64 steps (2048 K values) deep so that its partial-sum
+  // traffic stays small against its MFMA time.
+  const int64_t tiles = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
+  const int64_t steps = (K_rep * atom_k + 31) / 32;
+  int64_t s = tiles > 0 ? (256 + tiles - 1) / tiles : 1;
+  if (s > steps / 64) s = steps / 64;
+  if (s > 65535) s = 65535;
+  return int(s < 1 ? 1 : s);
+}
+
+int bmm_mma_tile_splitk(float* D, const uint32_t* A, const uint32_t* B, const float* C,
+                        float c_scalar, int64_t batch, int64_t M_rep, int64_t N_rep,
+                        int64_t K_rep, bmm_dtype dtype, int32_t atom_k, int32_t splits,
+                        float* workspace, int64_t workspace_bytes, void* stream) {
+  bmm::Status st = bmm::check_splitk(D, A, B, C, batch, M_rep, N_rep, K_rep, int(dtype), atom_k,
+                                     splits, workspace, workspace_bytes);
+  if (!st.ok()) return report(st);
+  if (batch == 0 || M_rep == 0 || N_rep == 0) return report(st);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t S = bmm::splitk_effective(K_rep, atom_k, splits);
+  const int64_t d_floats = batch * M_rep * N_rep * 128;
+  if (S > 0) {
+    // partial sums from zero, one per split, into the workspace
+    bmm::MmaArgs a{workspace, A, B, nullptr, 0.f, batch, M_rep, N_rep, K_rep, int(dtype), 0,
+                   1.f, 1.f, atom_k};
+    a.splits = int(S);
+    a.steps = (K_rep * atom_k + 31) / 32;
+    a.part_floats = d_floats;
+    const int rc = hip_status(bmm::launch_mma_tiled(a, s), "mma_tile_splitk tiled launch");
+    if (rc != BMM_OK) return rc;
+  }
+  return hip_status(bmm::launch_splitk_reduce(D, C, c_scalar, workspace, int(S), d_floats,
+                                              d_floats / 4, s),
+                    "mma_tile_splitk reduce launch");
 }
 
 int bmm_mma_tile(float* D, const uint32_t* A, const uint32_t* B, const float* C,

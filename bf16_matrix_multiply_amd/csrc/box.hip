@@ -1,4 +1,4 @@
-// Box copy through an LDS image: the role of the TMA tile-mode box load of the
+// Box transfers through an LDS image. The load: the role of the TMA tile-mode box load of the
 // cp.async.bulk.tensor page ("Operands and descriptor fields", "Example: two
 // explicit 8x16 boxes"), done the CDNA4 way. One workgroup stages one repeat:
 // its lanes read the box from global memory with consecutive lanes on
@@ -76,9 +76,82 @@ __global__ __launch_bounds__(kBoxThreads) void box_kernel(char* __restrict__ dst
   }
 }
 
-}  // namespace
+// ---- store and add reduction: compact image -> LDS image -> global box ----
+// The direction of the cp.async.bulk.tensor page's "Stores, reductions, and
+// completion": the same box contract, global destination first. One
+// workgroup takes one repeat: it stages the repeat's compact image into LDS
+// (swizzled as requested; coalesced reads), then writes every element whose
+// global coordinate lies inside the tensor, plain or added to what is there.
+// Within one launch no two lanes touch the same global element: the host
+// checks that the view does not overlap itself and launches repeats that
+// overlap one another in separate, stream-ordered launches.
 
-hipError_t launch_box(void* dst, const void* src, const bmm_box_desc& d, hipStream_t s) {
+// f32 -> bf16 bits, round to nearest even (NaN kept quiet, overflow to inf).
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return uint16_t((u >> 16) | 0x40u);
+  return uint16_t((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_value(uint16_t h) {
+  return __builtin_bit_cast(float, uint32_t(h) << 16);
+}
+
+// One rounding per add: f16 and bf16 sums are formed in f32 and rounded once
+// more to the 16-bit format; f32 has at least 2p+2 significand bits for both
+// formats, so the two roundings give the correctly rounded sum.
+template <int ET>
+__device__ __forceinline__ void add_elem(char* g, const char* v) {
+  if constexpr (ET == BMM_ELEM_F32) {
+    float* x = reinterpret_cast<float*>(g);
+    *x = *x + *reinterpret_cast<const float*>(v);
+  } else if constexpr (ET == BMM_ELEM_F16) {
+    _Float16* x = reinterpret_cast<_Float16*>(g);
+    *x = _Float16(float(*x) + float(*reinterpret_cast<const _Float16*>(v)));
+  } else if constexpr (ET == BMM_ELEM_BF16) {
+    uint16_t* x = reinterpret_cast<uint16_t*>(g);
+    *x = bf16_rne(bf16_value(*x) + bf16_value(*reinterpret_cast<const uint16_t*>(v)));
+  } else if constexpr (ET == BMM_ELEM_I32) {
+    uint32_t* x = reinterpret_cast<uint32_t*>(g);
+    *x = *x + *reinterpret_cast<const uint32_t*>(v);
+  } else {
+    uint64_t* x = reinterpret_cast<uint64_t*>(g);
+    *x = *x + *reinterpret_cast<const uint64_t*>(v);
+  }
+}
+
+// ET = 0: plain store of T-sized elements.
+template <typename T, int ET>
+__global__ __launch_bounds__(kBoxThreads) void box_store_kernel(char* __restrict__ dst,
+                                                                const char* __restrict__ img,
+                                                                BoxParams p, int64_t t0) {
+  extern __shared__ __attribute__((aligned(128))) char lds[];
+  const int64_t t = t0 + blockIdx.x;
+  const T* in = reinterpret_cast<const T*>(img) + t * p.box_elems;
+  for (int32_t e = threadIdx.x; e < p.box_elems; e += kBoxThreads)
+    *reinterpret_cast<T*>(lds + swizzle_offset(uint32_t(e) * sizeof(T), p.swizzle)) = in[e];
+  __syncthreads();
+  for (int32_t e = threadIdx.x; e < p.box_elems; e += kBoxThreads) {
+    int32_t rem = e;
+    bool inside = true;
+    int64_t off = 0;
+    for (int d = p.rank - 1; d >= 0; --d) {
+      const int32_t j = rem % p.box[d];
+      rem /= p.box[d];
+      const int64_t g = p.coords[d] + t * p.step[d] + j;
+      inside = inside && g >= 0 && g < p.dims[d];
+      off += g * p.strides[d];
+    }
+    if (!inside) continue;
+    const char* v = lds + swizzle_offset(uint32_t(e) * sizeof(T), p.swizzle);
+    if constexpr (ET == 0)
+      *reinterpret_cast<T*>(dst + off) = *reinterpret_cast<const T*>(v);
+    else
+      add_elem<ET>(dst + off, v);
+  }
+}
+
+BoxParams box_params(const bmm_box_desc& d) {
   BoxParams p{};
   p.rank = d.rank;
   p.eb = d.elem_bytes;
@@ -93,6 +166,49 @@ hipError_t launch_box(void* dst, const void* src, const bmm_box_desc& d, hipStre
     elems *= d.box[i];
   }
   p.box_elems = int32_t(elems);
+  return p;
+}
+
+}  // namespace
+
+hipError_t launch_box_store(void* dst, const void* img, const bmm_box_desc& d, int elem_type,
+                            bool repeats_disjoint, hipStream_t s) {
+  const BoxParams p = box_params(d);
+  const size_t lds_bytes = size_t((int64_t(p.box_elems) * d.elem_bytes + 127) / 128 * 128);
+  void (*kern)(char*, const char*, BoxParams, int64_t) = nullptr;
+  switch (elem_type) {
+    case BMM_ELEM_F32: kern = box_store_kernel<float, BMM_ELEM_F32>; break;
+    case BMM_ELEM_F16: kern = box_store_kernel<uint16_t, BMM_ELEM_F16>; break;
+    case BMM_ELEM_BF16: kern = box_store_kernel<uint16_t, BMM_ELEM_BF16>; break;
+    case BMM_ELEM_I32: kern = box_store_kernel<uint32_t, BMM_ELEM_I32>; break;
+    case BMM_ELEM_I64: kern = box_store_kernel<uint64_t, BMM_ELEM_I64>; break;
+    default:
+      switch (d.elem_bytes) {
+        case 1: kern = box_store_kernel<uint8_t, 0>; break;
+        case 2: kern = box_store_kernel<uint16_t, 0>; break;
+        case 4: kern = box_store_kernel<uint32_t, 0>; break;
+        default: kern = box_store_kernel<uint64_t, 0>; break;
+      }
+  }
+  char* out = static_cast<char*>(dst);
+  const char* in = static_cast<const char*>(img);
+  if (repeats_disjoint) {
+    hipLaunchKernelGGL(kern, dim3(unsigned(d.n_repeat)), dim3(kBoxThreads), lds_bytes, s, out, in,
+                       p, int64_t(0));
+    return hipGetLastError();
+  }
+  // overlapping repeats: one launch each, in repeat order
+  for (int64_t t = 0; t < d.n_repeat; ++t) {
+    hipLaunchKernelGGL(kern, dim3(1), dim3(kBoxThreads), lds_bytes, s, out, in, p, t);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_box(void* dst, const void* src, const bmm_box_desc& d, hipStream_t s) {
+  const BoxParams p = box_params(d);
+  const int64_t elems = p.box_elems;
   // The swizzle keeps every offset inside its 128-byte row: round the image up.
   const size_t lds_bytes = size_t((elems * d.elem_bytes + 127) / 128 * 128);
   hipLaunchKernelGGL(box_kernel, dim3(unsigned(d.n_repeat)), dim3(kBoxThreads), lds_bytes, s,

@@ -22,6 +22,10 @@ struct MmaArgs {
   float alpha, beta;
   // atom K of the packed operands: 16 (m16n8k16 layout) or 8 (m16n8k8)
   int atom_k;
+  // split-K (tiled kernel only): splits > 1 cuts the `steps` 32-value K steps
+  // into that many ranges, partial sums from zero to D + s * part_floats
+  int splits;
+  int64_t steps, part_floats;
 };
 
 // In 8-value K chunks, one 32-deep MFMA step spans the same bytes in either
@@ -41,11 +45,18 @@ hipError_t launch_pack(uint32_t* dst, const uint16_t* src, int64_t batch, int64_
 hipError_t launch_pack_kmajor(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
                               int64_t K, int64_t ld, int R, hipStream_t s);
 hipError_t launch_box(void* dst, const void* src, const bmm_box_desc& d, hipStream_t s);
+// Store (elem_type 0) or add reduction of a compact image into a global box.
+hipError_t launch_box_store(void* dst, const void* img, const bmm_box_desc& d, int elem_type,
+                            bool repeats_disjoint, hipStream_t s);
 hipError_t launch_mma_direct(const MmaArgs& a, hipStream_t s);
 // The tiled kernel addresses one tile's operands with 32-bit buffer offsets:
 // it takes K < 2^22.
 constexpr int64_t kTiledMaxK = int64_t(1) << 22;
 hipError_t launch_mma_tiled(const MmaArgs& a, hipStream_t s);
 hipError_t launch_mma_skinny(const MmaArgs& a, hipStream_t s);
+// D = C (or c) + part[0] + part[1] + ... + part[splits-1], added in that order;
+// n4 = floats of D / 4, part s at parts + s * part_floats.
+hipError_t launch_splitk_reduce(float* D, const float* C, float c, const float* parts,
+                                int splits, int64_t part_floats, int64_t n4, hipStream_t s);
 
 }  // namespace bmm

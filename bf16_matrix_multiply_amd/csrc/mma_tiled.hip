@@ -147,14 +147,25 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
   const int kj = wave & 1;
   const int cs = 2 * kj + (lane >> 5);
   const int64_t nck = k_chunks(p);
+  // Split-K: split s = blockIdx.y sums the 32-value steps
+  // [s * steps / S, (s + 1) * steps / S) and writes its partial sum to
+  // D + s * part_floats; without splits the whole K goes to D.
+  int64_t kc0 = 0, kcn = nck;  // first 8-value chunk and chunk count of this split
+  float* const Dout = p.splits > 1 ? p.D + int64_t(blockIdx.y) * p.part_floats : p.D;
+  if (p.splits > 1) {
+    const int64_t sp = blockIdx.y;
+    kc0 = 4 * (sp * p.steps / p.splits);
+    const int64_t kc1 = 4 * ((sp + 1) * p.steps / p.splits);
+    kcn = (kc1 < nck ? kc1 : nck) - kc0;
+  }
   const int64_t a_row_bytes = nck * 256, b_row_bytes = nck * 128;
-  const int64_t a_left = (p.M_rep - m_atom0) * a_row_bytes;
-  const int64_t b_left = (p.N_rep - n_atom0) * b_row_bytes;
+  const int64_t a_left = (p.M_rep - m_atom0) * a_row_bytes - kc0 * 256;
+  const int64_t b_left = (p.N_rep - n_atom0) * b_row_bytes - kc0 * 128;
   const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(p.A + (tc.b * p.M_rep + m_atom0) * nck * 64), 0,
+      const_cast<uint32_t*>(p.A + (tc.b * p.M_rep + m_atom0) * nck * 64 + kc0 * 64), 0,
       int(a_left < kOutOfRange ? a_left : kOutOfRange), kBufferFlags);
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint32_t*>(p.B + (tc.b * p.N_rep + n_atom0) * nck * 32), 0,
+      const_cast<uint32_t*>(p.B + (tc.b * p.N_rep + n_atom0) * nck * 32 + kc0 * 32), 0,
       int(b_left < kOutOfRange ? b_left : kOutOfRange), kBufferFlags);
   uint32_t a_voff[kLoadsA], b_voff[kLoadsB];
 #pragma unroll
@@ -177,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
   // the test is uniform over the wave.
   auto issue = [&](Stage& st, int64_t k) {
     const uint32_t koff_a = uint32_t(k * 1024), koff_b = uint32_t(k * 512);
-    const bool k_ok = KA == 16 ? 4 * k + 2 * kj < nck : 4 * k + cs < nck;
+    const bool k_ok = KA == 16 ? 4 * k + 2 * kj < kcn : 4 * k + cs < kcn;
 #pragma unroll
     for (int r = 0; r < kLoadsA; ++r)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -298,7 +309,7 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
     }
     __builtin_amdgcn_sched_group_barrier(0x008, kWaveBlocksM * kWaveBlocksN - kLoadsPerSlab, 0);
   };
-  const int64_t n_slabs = (nck + 3) / 4;
+  const int64_t n_slabs = (kcn + 3) / 4;
   for (int64_t s = 0; s < n_slabs; s += kStages) {
     slab(s + 0, st0, st1, fb[0], fa[0], fb[1], fa[1]);
     slab(s + 1, st1, st2, fb[1], fa[1], fb[0], fa[0]);
@@ -317,13 +328,13 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
       for (int q = 0; q < 4; ++q) {
         f32x4 v = {acc[pm][qn][4 * q + 0], acc[pm][qn][4 * q + 1], acc[pm][qn][4 * q + 2],
                    acc[pm][qn][4 * q + 3]};
-        float* dst = p.D + d_lane + 2 * pm * d_mstride + (4 * qn + q) * kAtomFloats;
+        float* dst = Dout + d_lane + 2 * pm * d_mstride + (4 * qn + q) * kAtomFloats;
         const bool ok =
             interior || (lane_row_atom + 2 * pm < p.M_rep && lane_col_atom + 4 * qn + q < p.N_rep);
         if constexpr (kScaled) {
           f32x4 cv = {p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
           if constexpr (kHasC) {
-            if (ok) cv = load16f(p.C + (dst - p.D));
+            if (ok) cv = load16f(p.C + (dst - Dout));
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.alpha, v[e], p.beta * cv[e]);
@@ -354,7 +365,9 @@ hipError_t launch_mma_tiled(const MmaArgs& a, hipStream_t s) {
   };
   auto kern = a.dtype == kBF16 ? pick_ka(std::integral_constant<int, kBF16>{})
                                : pick_ka(std::integral_constant<int, kF16>{});
-  hipLaunchKernelGGL(kern, dim3(unsigned(n_tiles)), dim3(kThreads), 0, s, a, n_tiles, MT, NT);
+  const unsigned splits = a.splits > 1 ? unsigned(a.splits) : 1u;
+  hipLaunchKernelGGL(kern, dim3(unsigned(n_tiles), splits), dim3(kThreads), 0, s, a, n_tiles, MT,
+                     NT);
   return hipGetLastError();
 }
 

@@ -1,6 +1,7 @@
 #include "validate.h"
 
 #include <cstdio>
+#include <string>
 
 namespace bmm {
 namespace {
@@ -104,55 +105,107 @@ Status check_pack_kmajor(const uint32_t* dst, const uint16_t* src, int64_t batch
   return Status{};
 }
 
-Status check_box(const void* dst, const void* src, const bmm_box_desc* d) {
-  if (!d) return fail(BMM_EINVAL, "box_copy: null descriptor");
-  if (d->rank < 1 || d->rank > 5) return fail(BMM_EINVAL, "box_copy: rank %lld not in 1..5", d->rank);
+// Descriptor fields shared by the load, the store and the add reduction.
+// On success *span is the byte extent of the global view (from its base) and
+// *image the bytes of one repeat's image.
+Status check_box_desc(const bmm_box_desc* d, const char* what, int64_t* span_out,
+                      int64_t* image_out) {
+  auto failw = [what](int code, const char* fmt, long long a = 0, long long b = 0) {
+    Status s = fail(code, fmt, a, b);
+    s.msg = std::string(what) + ": " + s.msg;
+    return s;
+  };
+  if (!d) return failw(BMM_EINVAL, "null descriptor");
+  if (d->rank < 1 || d->rank > 5) return failw(BMM_EINVAL, "rank %lld not in 1..5", d->rank);
   const int eb = d->elem_bytes;
   if (eb != 1 && eb != 2 && eb != 4 && eb != 8)
-    return fail(BMM_EINVAL, "box_copy: elem_bytes %lld not 1, 2, 4 or 8", eb);
+    return failw(BMM_EINVAL, "elem_bytes %lld not 1, 2, 4 or 8", eb);
   if (d->swizzle < 0 || d->swizzle > 3)
-    return fail(BMM_EINVAL, "box_copy: swizzle %lld not in 0..3", d->swizzle);
+    return failw(BMM_EINVAL, "swizzle %lld not in 0..3", d->swizzle);
   if (d->oob_fill != 0)
-    return fail(BMM_EINVAL, "box_copy: oob_fill %lld unsupported (only 0 = zero fill)",
-                d->oob_fill);
-  if (d->n_repeat < 1) return fail(BMM_EINVAL, "box_copy: n_repeat %lld < 1", d->n_repeat);
+    return failw(BMM_EINVAL, "oob_fill %lld unsupported (only 0 = zero fill)", d->oob_fill);
+  if (d->n_repeat < 1) return failw(BMM_EINVAL, "n_repeat %lld < 1", d->n_repeat);
   int64_t box_elems = 1, span = 0;
   for (int i = 0; i < d->rank; ++i) {
     if (d->box[i] < 1 || d->box[i] > 256)
-      return fail(BMM_EINVAL, "box_copy: box[%lld] = %lld not in 1..256", i, d->box[i]);
+      return failw(BMM_EINVAL, "box[%lld] = %lld not in 1..256", i, d->box[i]);
     if (d->dims[i] < 1 || d->dims[i] > kMaxExtent)
-      return fail(BMM_EINVAL, "box_copy: dims[%lld] = %lld out of range", i, d->dims[i]);
+      return failw(BMM_EINVAL, "dims[%lld] = %lld out of range", i, d->dims[i]);
     const int64_t c = d->coords[i], st = d->coord_step[i];
     if (c < -kMaxExtent || c > kMaxExtent || st < -kMaxExtent || st > kMaxExtent)
-      return fail(BMM_EINVAL, "box_copy: coords/coord_step[%lld] out of range", i);
+      return failw(BMM_EINVAL, "coords/coord_step[%lld] out of range", i);
     box_elems *= d->box[i];
     if (i == d->rank - 1) {
       if (d->strides[i] != eb)
-        return fail(BMM_EINVAL, "box_copy: innermost stride %lld must equal elem_bytes %lld",
-                    d->strides[i], eb);
+        return failw(BMM_EINVAL, "innermost stride %lld must equal elem_bytes %lld",
+                     d->strides[i], eb);
     } else {
       if (d->strides[i] <= 0 || d->strides[i] > kMaxBytes)
-        return fail(BMM_EINVAL, "box_copy: stride[%lld] = %lld must be positive", i,
-                    d->strides[i]);
+        return failw(BMM_EINVAL, "stride[%lld] = %lld must be positive", i, d->strides[i]);
       if (d->strides[i] % 16)
-        return fail(BMM_EALIGN, "box_copy: outer stride[%lld] = %lld not a multiple of 16", i,
-                    d->strides[i]);
+        return failw(BMM_EALIGN, "outer stride[%lld] = %lld not a multiple of 16", i,
+                     d->strides[i]);
     }
     int64_t s = mul_capped({d->dims[i] - 1, d->strides[i]});
-    if (s < 0 || span + s > kMaxBytes) return fail(BMM_EINVAL, "box_copy: tensor too large");
+    if (s < 0 || span + s > kMaxBytes) return failw(BMM_EINVAL, "tensor too large");
     span += s;
   }
   span += eb;
   const int64_t image = box_elems * eb;
   if (image > kBoxImageLimit)
-    return fail(BMM_ERANGE, "box_copy: one repeat's image is %lld bytes, limit %lld", image,
-                kBoxImageLimit);
+    return failw(BMM_ERANGE, "one repeat's image is %lld bytes, limit %lld", image,
+                 kBoxImageLimit);
+  *span_out = span;
+  *image_out = image;
+  return Status{};
+}
+
+Status check_box(const void* dst, const void* src, const bmm_box_desc* d) {
+  int64_t span = 0, image = 0;
+  Status st = check_box_desc(d, "box_copy", &span, &image);
+  if (!st.ok()) return st;
   if (!dst || !src) return fail(BMM_EINVAL, "box_copy: null pointer");
   if (!aligned16(dst) || !aligned16(src))
     return fail(BMM_EALIGN, "box_copy: dst_image and src must be 16-byte aligned");
   const int64_t total = mul_capped({image, d->n_repeat});
   if (total < 0) return fail(BMM_EINVAL, "box_copy: image too large");
   if (overlaps(dst, total, src, span)) return fail(BMM_EOVERLAP, "box_copy: dst overlaps src");
+  return Status{};
+}
+
+Status check_box_store(const void* dst, const void* img, const bmm_box_desc* d,
+                       int32_t elem_type, const char* what) {
+  int64_t span = 0, image = 0;
+  Status st = check_box_desc(d, what, &span, &image);
+  if (!st.ok()) return st;
+  auto failw = [what](int code, const char* fmt, long long a = 0, long long b = 0) {
+    Status s = fail(code, fmt, a, b);
+    s.msg = std::string(what) + ": " + s.msg;
+    return s;
+  };
+  if (elem_type != 0) {
+    static const int kTypeBytes[6] = {0, 4, 2, 2, 4, 8};
+    if (elem_type < BMM_ELEM_F32 || elem_type > BMM_ELEM_I64)
+      return failw(BMM_EINVAL, "elem_type %lld is not a bmm_elem_type", elem_type);
+    if (kTypeBytes[elem_type] != d->elem_bytes)
+      return failw(BMM_EINVAL, "elem_type %lld does not match elem_bytes %lld", elem_type,
+                   d->elem_bytes);
+  }
+  // Every global element of the view must have its own address: each outer
+  // stride covers the whole extent of the dimensions inside it.
+  int64_t inner = d->elem_bytes;
+  for (int i = d->rank - 1; i >= 0; --i) {
+    if (i < d->rank - 1 && d->dims[i] > 1 && d->strides[i] < inner)
+      return failw(BMM_EINVAL, "stride[%lld] = %lld makes the destination view overlap itself",
+                   i, d->strides[i]);
+    inner = (d->dims[i] - 1) * d->strides[i] + inner;
+  }
+  if (!dst || !img) return failw(BMM_EINVAL, "null pointer");
+  if (!aligned16(dst) || !aligned16(img))
+    return failw(BMM_EALIGN, "dst and src_image must be 16-byte aligned");
+  const int64_t total = mul_capped({image, d->n_repeat});
+  if (total < 0) return failw(BMM_EINVAL, "image too large");
+  if (overlaps(dst, span, img, total)) return failw(BMM_EOVERLAP, "dst overlaps src_image");
   return Status{};
 }
 
@@ -183,6 +236,45 @@ Status check_mma(const float* D, const uint32_t* A, const uint32_t* B, const flo
   if (overlaps(D, d_bytes, B, b_bytes)) return fail(BMM_EOVERLAP, "mma_tile: D overlaps B");
   if (C && C != D && overlaps(D, d_bytes, C, d_bytes))
     return fail(BMM_EOVERLAP, "mma_tile: D partially overlaps C (only D == C is allowed)");
+  return Status{};
+}
+
+int64_t splitk_effective(int64_t K_rep, int32_t atom_k, int32_t splits) {
+  const int64_t steps = (K_rep * atom_k + 31) / 32;
+  return splits < steps ? splits : steps;
+}
+
+Status check_splitk(const float* D, const uint32_t* A, const uint32_t* B, const float* C,
+                    int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep, int32_t dtype,
+                    int32_t atom_k, int32_t splits, const void* workspace,
+                    int64_t workspace_bytes) {
+  Status st = check_mma(D, A, B, C, batch, M_rep, N_rep, K_rep, dtype, BMM_KERNEL_TILED, atom_k);
+  if (!st.ok()) {
+    st.msg = "mma_tile_splitk: " + st.msg;
+    return st;
+  }
+  if (splits < 1 || splits > 65535)
+    return fail(BMM_EINVAL, "mma_tile_splitk: splits %lld not in 1..65535", splits);
+  if (K_rep * atom_k >= (int64_t(1) << 22))
+    return fail(BMM_EINVAL, "mma_tile_splitk: K = %lld values, the tiled kernel takes K < 2^22",
+                K_rep * atom_k);
+  const int64_t d_bytes = mul_capped({batch, M_rep, N_rep, 512});
+  if (d_bytes == 0) return Status{};
+  const int64_t need = mul_capped({splitk_effective(K_rep, atom_k, splits), d_bytes});
+  if (need < 0) return fail(BMM_EINVAL, "mma_tile_splitk: workspace too large");
+  if (workspace_bytes < need)
+    return fail(BMM_EINVAL, "mma_tile_splitk: workspace_bytes %lld < %lld needed",
+                workspace_bytes, need);
+  if (need > 0) {
+    if (!workspace) return fail(BMM_EINVAL, "mma_tile_splitk: workspace is null");
+    if (!aligned16(workspace))
+      return fail(BMM_EALIGN, "mma_tile_splitk: workspace must be 16-byte aligned");
+    const int64_t a_bytes = mul_capped({batch, M_rep, K_rep, 32 * atom_k});
+    const int64_t b_bytes = mul_capped({batch, N_rep, K_rep, 16 * atom_k});
+    if (overlaps(workspace, need, D, d_bytes) || overlaps(workspace, need, A, a_bytes) ||
+        overlaps(workspace, need, B, b_bytes) || (C && overlaps(workspace, need, C, d_bytes)))
+      return fail(BMM_EOVERLAP, "mma_tile_splitk: workspace overlaps D, A, B or C");
+  }
   return Status{};
 }
 

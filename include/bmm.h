@@ -18,7 +18,8 @@
  *     choice or transpose).
  *   - Return value: BMM_OK (0) or a negative status; bmm_last_error()
  *     returns a message for the last failure on the calling thread.
- *   - The library allocates no device memory and keeps no device state.
+ *   - The library allocates no device memory and keeps no device state;
+ *     scratch space (the split-K partial sums) is a caller-owned workspace.
  *   - Destination first (mma.sync page, "Operand coordinates and
  *     ownership": the call takes D, A, B, C).
  */
@@ -165,6 +166,56 @@ int bmm_box_copy(void* dst_image, const void* src, const bmm_box_desc* desc,
                  int64_t* bytes_moved, void* stream);
 
 /*
+ * bmm_box_store — a compact image written into a rectangular global box.
+ *
+ * The store direction of the cp.async.bulk.tensor page ("Stores, reductions,
+ * and completion": the load's coordinate/box contract, global destination
+ * first). Each repeat's image is staged through an LDS image (with the
+ * requested swizzle) and written out:
+ *
+ *   dst[coords + t*coord_step + j] = src_image[t, j_0..j_{rank-1}]
+ *                                    for every coordinate inside dims;
+ *   elements outside dims are not written.
+ *
+ * Repeats are applied in ascending t: where the boxes of two repeats
+ * overlap, the later repeat's values stand.
+ * desc         as bmm_box_copy; additionally the destination view must not
+ *              overlap itself (each outer stride at least the byte extent of
+ *              the dimensions inside it), else BMM_EINVAL.
+ * src_image    (n_repeat, box...) compact, 16-byte aligned, not overlapping dst.
+ * bytes_moved  nullable; receives n_repeat * prod(box) * elem_bytes (image bytes read).
+ * Errors: BMM_EINVAL, BMM_EALIGN, BMM_EOVERLAP, BMM_ERANGE, BMM_EHIP.
+ */
+int bmm_box_store(void* dst, const void* src_image, const bmm_box_desc* desc,
+                  int64_t* bytes_moved, void* stream);
+
+/* Element types of bmm_box_reduce_add; each must match desc->elem_bytes. */
+typedef enum {
+  BMM_ELEM_F32 = 1,  /* 4 bytes */
+  BMM_ELEM_F16 = 2,  /* 2 bytes, IEEE binary16 */
+  BMM_ELEM_BF16 = 3, /* 2 bytes, bfloat16 */
+  BMM_ELEM_I32 = 4,  /* 4 bytes, wraps modulo 2^32 (signed or unsigned alike) */
+  BMM_ELEM_I64 = 5   /* 8 bytes, wraps modulo 2^64 */
+} bmm_elem_type;
+
+/*
+ * bmm_box_reduce_add — add a compact image into a rectangular global box.
+ *
+ * The add reduction of the cp.async.bulk.tensor page ("Stores, reductions,
+ * and completion"); the destination holds its starting value beforehand.
+ *
+ *   dst[coords + t*coord_step + j] = dst[...] + src_image[t, j]
+ *
+ * for every coordinate inside dims, repeats in ascending t, one rounding per
+ * add in the element type (round to nearest even; f16 and bf16 sums are
+ * correctly rounded). Arguments, ordering and errors as bmm_box_store, plus
+ * BMM_EINVAL for an elem_type that is not a bmm_elem_type or does not match
+ * elem_bytes. NaN payloads of float results are unspecified.
+ */
+int bmm_box_reduce_add(void* dst, const void* src_image, const bmm_box_desc* desc,
+                       int32_t elem_type, int64_t* bytes_moved, void* stream);
+
+/*
  * bmm_mma_tile — D = A * B^T + C over packed operands.
  *
  * Defined by the mma.sync page: "Operand coordinates and ownership" (the
@@ -245,6 +296,44 @@ typedef struct {
 int bmm_mma_tile_opts(float* D, const uint32_t* A, const uint32_t* B, const float* C,
                       float c_scalar, int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep,
                       bmm_dtype dtype, const bmm_mma_opts* opts, void* stream);
+
+/*
+ * bmm_mma_tile_splitk — the multiply-accumulate with K split across workgroups.
+ *
+ * For shapes with few output tiles and a long K. The K axis is cut at
+ * multiples of 32 values into S = min(splits, ceil(K / 32)) balanced ranges
+ * of whole 32-value steps: split s takes steps [s*n/S, (s+1)*n/S) of the
+ * n = ceil(K / 32). Each split's partial sum P_s starts from zero; then the
+ * partial sums are add-reduced into a destination that starts at C (the
+ * cp.async.bulk.tensor page, "Stores, reductions, and completion": the
+ * reduction destination is initialised to the intended starting value):
+ *
+ *   D = (((C + P_0) + P_1) + ...) + P_{S-1}      (fp32, in this order)
+ *
+ * so the result is the same on every run and for every schedule. K = 0
+ * gives D = C.
+ * D, A, B, C, c_scalar, extents, dtype: as bmm_mma_tile (in place D == C
+ * allowed); atom_k 16 or 8 as in bmm_mma_tile_opts; K < 2^22 values.
+ * splits     1..65535 (bmm_splitk_default suggests one).
+ * workspace  device memory of at least bmm_mma_splitk_workspace_bytes(...)
+ *            bytes (S * batch * M_rep * N_rep * 512), 16-byte aligned, not
+ *            overlapping D, A, B or C; owned by the caller, clobbered.
+ * Errors: as bmm_mma_tile_with; BMM_EINVAL also for splits, K and a missing
+ * or short workspace, BMM_EOVERLAP for an overlapping workspace.
+ */
+int bmm_mma_tile_splitk(float* D, const uint32_t* A, const uint32_t* B, const float* C,
+                        float c_scalar, int64_t batch, int64_t M_rep, int64_t N_rep,
+                        int64_t K_rep, bmm_dtype dtype, int32_t atom_k, int32_t splits,
+                        float* workspace, int64_t workspace_bytes, void* stream);
+
+/* Workspace bytes bmm_mma_tile_splitk needs (0 when K = 0), or < 0. */
+int64_t bmm_mma_splitk_workspace_bytes(int64_t batch, int64_t M_rep, int64_t N_rep,
+                                       int64_t K_rep, int32_t atom_k, int32_t splits);
+
+/* A split count for bmm_mma_tile_splitk: enough tiles x splits for every CU,
+ * each split at least 2048 K values deep; 1 when splitting does not pay. */
+int bmm_splitk_default(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep,
+                       int32_t atom_k);
 
 /* Which kernel AUTO would run for this shape (K_rep in 16-deep atoms; a
  * bmm_kernel value), or < 0. */

@@ -248,3 +248,77 @@ def test_mma_opts_sizes_operands_by_atom_k(L):
     k8 = bmm.MmaOpts(8, 1, 0, 1.0, 1.0)
     assert mma_opts(L, D=D, C=D + 512, opts=k16) == EOVERLAP and "overlaps A" in err(L)
     assert mma_opts(L, D=D, C=D + 512, opts=k8) == EOVERLAP and "partially overlaps C" in err(L)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(rank=0), EINVAL, "rank"),
+    (dict(box=(1, 300)), EINVAL, "box[1]"),
+    (dict(oob_fill=2), EINVAL, "oob_fill"),
+    (dict(strides=(0, 32)), EINVAL, "overlap itself"),     # 16 columns of 4 B need 64
+    (dict(strides=(0, 72)), EALIGN, "multiple of 16"),
+])
+def test_box_store_rejects_desc(L, kw, code, needle):
+    d = box_desc(**kw)
+    n = ctypes.c_int64(-7)
+    assert L.bmm_box_store(P0, P1, ctypes.byref(d), ctypes.byref(n), None) == code
+    assert needle in err(L) and err(L).startswith("box_store")
+    assert n.value == -7
+
+
+def test_box_store_rejects_pointers(L):
+    d = box_desc()
+    assert L.bmm_box_store(P0 + 8, P1, ctypes.byref(d), None, None) == EALIGN
+    assert L.bmm_box_store(0, P1, ctypes.byref(d), None, None) == EINVAL
+    assert L.bmm_box_store(P1 + 512, P1, ctypes.byref(d), None, None) == EOVERLAP
+    assert L.bmm_box_store(P0, P1, None, None, None) == EINVAL
+
+
+@pytest.mark.parametrize("etype,eb,needle", [
+    (0, 4, "not a bmm_elem_type"),
+    (6, 4, "not a bmm_elem_type"),
+    (2, 4, "does not match elem_bytes"),     # f16 over 4-byte elements
+    (5, 4, "does not match elem_bytes"),
+    (1, 8, "does not match elem_bytes"),
+])
+def test_box_reduce_rejects_types(L, etype, eb, needle):
+    d = box_desc(elem_bytes=eb, strides=(1, eb))
+    assert L.bmm_box_reduce_add(P0, P1, ctypes.byref(d), etype, None, None) == EINVAL
+    assert needle in err(L) and err(L).startswith("box_reduce_add")
+
+
+def splitk(L, D=P0, A=P1, B=P2, C=None, batch=1, M=2, N=3, K=4, dtype=1, atom_k=16, splits=2,
+           ws=P3, ws_bytes=1 << 20):
+    return L.bmm_mma_tile_splitk(D, A, B, C, 0.0, batch, M, N, K, dtype, atom_k, splits, ws,
+                                 ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(splits=0), EINVAL, "splits"),
+    (dict(splits=70000), EINVAL, "splits"),
+    (dict(atom_k=4), EINVAL, "atom_k"),
+    (dict(dtype=5), EINVAL, "dtype"),
+    (dict(K=1 << 18), EINVAL, "K < 2^22"),
+    (dict(ws_bytes=100), EINVAL, "workspace_bytes"),
+    (dict(ws=0), EINVAL, "workspace is null"),
+    (dict(ws=P3 + 8), EALIGN, "workspace"),
+    (dict(ws=P1 + 256), EOVERLAP, "workspace overlaps"),
+    (dict(ws=P0 + 512), EOVERLAP, "workspace overlaps"),
+    (dict(D=P0 + 4), EALIGN, "aligned"),
+])
+def test_splitk_rejects(L, kw, code, needle):
+    assert splitk(L, **kw) == code
+    assert needle in err(L) and err(L).startswith("mma_tile_splitk")
+
+
+def test_splitk_workspace_and_default(L):
+    # S = min(splits, ceil(K / 32)): K = 64 values -> 2 steps
+    assert L.bmm_mma_splitk_workspace_bytes(1, 2, 3, 4, 16, 5) == 2 * 2 * 3 * 512
+    assert L.bmm_mma_splitk_workspace_bytes(1, 2, 3, 4, 8, 5) == 1 * 2 * 3 * 512
+    assert L.bmm_mma_splitk_workspace_bytes(1, 2, 3, 0, 16, 5) == 0
+    assert L.bmm_mma_splitk_workspace_bytes(1, 2, 3, 4, 16, 0) == EINVAL
+    # 1024 x 1024 x 65536: 16 tiles -> 16 splits; 8192^3: 1024 tiles -> 1
+    assert L.bmm_splitk_default(1, 64, 128, 4096, 16) == 16
+    assert L.bmm_splitk_default(1, 512, 1024, 512, 16) == 1
+    assert L.bmm_splitk_default(1, 1, 1, 10, 16) == 1
+    # empty problems need no workspace and launch nothing
+    assert splitk(L, D=0, A=0, B=0, M=0, ws=0, ws_bytes=0) == 0

@@ -106,6 +106,16 @@ WORKLOADS = {
     ]
 }
 
+# Beyond the five: a long-K problem with few output tiles (16 tiles of 256 x 256
+# for 256 CUs), the shape the split-K form is for.
+EXTRA_WORKLOADS = {
+    w.name: w
+    for w in [
+        Workload("deep_k_1024x1024x65536_bf16_ctensor", 1, 1024, 1024, 65536, BF16, "normal",
+                 "normal", c_tensor=True),
+    ]
+}
+
 # The headline compute-bound workload that bench.py times.
 HEADLINE = "gemm_8192_bf16_ctensor"
 SKINNY = "skinny_16x16384x16384_bf16"
