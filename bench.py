@@ -208,6 +208,27 @@ def main():
         f"pack A {pa.mean()*1e3:.1f} us, pack B {pb.mean()*1e3:.1f} us, "
         f"mma_tile[{kernel}] {mm.mean()*1e3:.1f} us (min {mm.min()*1e3:.1f})")
 
+    # HBM-bound multiply: also time it with the caches flushed (a 2 GiB fill
+    # between calls evicts L2 and the 256 MB Infinity Cache), so no part of B
+    # is served from a cache the step's own pack just filled.
+    cold_us = None
+    if w.flops / w.algorithmic_bytes < RIDGE_FLOP_PER_BYTE:
+        flush = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(10):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            bmm.mma_tile(A, B, C, c, w.dtype, out=D, kernel=kernel, alpha=args.alpha,
+                         beta=args.beta)
+            e1.record(stream)
+            cold.append((e0, e1))
+        torch.cuda.synchronize()
+        cold_us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in cold]))
+        del flush
+        log(f"[bench] mma_tile after a cache flush: {cold_us:.1f} us "
+            f"({w.algorithmic_bytes / cold_us / 1e3:.0f} GB/s)")
+
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     op_bytes = 2 * (w.batch * w.M * w.K * 2)          # pack A: read + write
     op_bytes_b = 2 * (w.batch * w.N * w.K * 2)        # pack B: read + write
@@ -250,7 +271,10 @@ def main():
                     "mma_tile_tflops": round(w.flops / mma_s / 1e12, 2),
                     "mma_tile_gbs": round(w.algorithmic_bytes / mma_s / 1e9, 1),
                     "pack_gbs": round((op_bytes + op_bytes_b) / ((pa.mean() + pb.mean()) * 1e-3)
-                                      / 1e9, 1)},
+                                      / 1e9, 1),
+                    "mma_tile_cold_us": None if cold_us is None else round(cold_us, 2),
+                    "mma_tile_cold_gbs": None if cold_us is None
+                    else round(w.algorithmic_bytes / cold_us / 1e3, 1)},
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

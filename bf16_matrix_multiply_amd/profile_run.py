@@ -14,7 +14,8 @@ workload's synthetic inputs.
         --workload gemm_8192_bf16_ctensor --kernel mma_tile
 
 turns the counter CSVs of a FETCH_SIZE and a WRITE_SIZE pass into the
-per-launch HBM byte record that bench.py reports as ``traffic``.
+per-launch HBM byte record that bench.py reports as ``traffic`` (for packing:
+per step, the A and B launches together).
 """
 from __future__ import annotations
 
@@ -28,7 +29,7 @@ import sys
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 COPY_BYTES = 1 << 30   # calibration copy: 1 GiB read + 1 GiB written
 KERNEL_SOURCES = {
-    "mma_tile": ["mma_direct.hip", "mma_tiled.hip", "mma_skinny.hip", "common.h"],
+    "mma_tile": ["mma_direct.hip", "mma_tiled.hip", "mma_skinny.hip", "common.h", "launch.h"],
     "pack_operand": ["pack.hip", "common.h"],
 }
 KERNEL_MATCH = {"mma_tile": "mma_", "pack_operand": "pack_kernel"}
@@ -111,7 +112,10 @@ def summarize(fetch_csv, write_csv, workload, kernel):
         copy_kib = d[copy_ids[0]][1]
         scale = (COPY_BYTES / 1024) / copy_kib if copy_kib > 0 else float("nan")
         mine = [v for i, (n, v) in d.items() if KERNEL_MATCH[kernel] in n]
-        kib = sum(mine) / len(mine)
+        # one launch of the multiply per step; packing is two launches per
+        # step (A and B), counted together as bench.py's pack roofline does
+        per_step = 1 if kernel == "mma_tile" else 2
+        kib = sum(mine) / (len(mine) / per_step)
         rec[f"{key}_kib_per_dispatch_raw"] = round(kib, 1)
         rec[f"{key}_copy_kib_raw"] = round(copy_kib, 1)
         rec[f"{key}_scale"] = round(scale, 4)
