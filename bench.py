@@ -119,6 +119,9 @@ def main():
     ap.add_argument("--atom-k", type=int, default=16, choices=[16, 8],
                     help="K depth of a packed atom: 16, or 8 for the m16n8k8 layout "
                          "(pack_operand_k8 + mma_tile_opts)")
+    ap.add_argument("--context", action="store_true",
+                    help="also time torch.matmul (the vendor library) on the same logical operands, "
+                         "for context only")
     ap.add_argument("--splitk", type=int, default=None,
                     help="run the split-K form with this many splits (0: the library's default)")
     args = ap.parse_args()
@@ -229,6 +232,31 @@ def main():
         log(f"[bench] mma_tile after a cache flush: {cold_us:.1f} us "
             f"({w.algorithmic_bytes / cold_us / 1e3:.0f} GB/s)")
 
+    context = None
+    if args.context and w.dtype == "bf16" and w.batch == 1 and not args.kmajor:
+        # Context, not a target: the vendor library on the same row-major
+        # halves, D = A B^T (no C), bf16 output and float32 output.
+        at, bt = a[0].view(torch.bfloat16), b[0].view(torch.bfloat16).t()
+        context = {"note": "torch.matmul on the same operands (A B^T, no C); not this path"}
+        forms = {"bf16_out": lambda: torch.matmul(at, bt),
+                 "f32_out": lambda: torch.mm(at, bt, out_dtype=torch.float32)}
+        for key, fn in forms.items():
+            try:
+                for _ in range(3):
+                    fn()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(10):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / 10
+                context[key] = {"us": round(us, 1), "tflops": round(w.flops / us / 1e6, 1)}
+            except (RuntimeError, TypeError) as e:
+                context[key] = f"unavailable: {str(e)[:80]}"
+        log(f"[bench] context: {context}")
+
     value = w.flops / (ms_per_step * 1e-3) / 1e12
     op_bytes = 2 * (w.batch * w.M * w.K * 2)          # pack A: read + write
     op_bytes_b = 2 * (w.batch * w.N * w.K * 2)        # pack B: read + write
@@ -277,6 +305,8 @@ def main():
                     else round(w.algorithmic_bytes / cold_us / 1e3, 1)},
         "cpu_baseline": None,
     }
+    if context is not None:
+        line["context"] = context
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample of the same workload")
         line["cpu_baseline"] = cpu_baseline(w, inp, D.cpu().numpy(), args.cpu_seconds, args.alpha,

@@ -56,4 +56,15 @@ __device__ __forceinline__ void store16f(float* p, f32x4 v) {
   *reinterpret_cast<f32x4*>(p) = v;
 }
 
+// Streaming forms for data touched once (C read, D written): non-temporal,
+// so they do not push the operand tiles other workgroups still need out of
+// the caches.
+__device__ __forceinline__ f32x4 load16f_nt(const float* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+}
+
+__device__ __forceinline__ void store16f_nt(float* p, f32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p));
+}
+
 }  // namespace bmm

@@ -40,7 +40,8 @@
 // registers; wait for its own loads of the next slab and its fragment reads;
 // barrier; issue the loads of slab s+4; read the next slab's fragments; the
 // MFMAs of the second K atom. The barrier is a bare s_barrier after a counted
-// wait, so the loads of later slabs stay in flight across it.
+// wait, so the loads of later slabs stay in flight across it. C is read and D
+// written with non-temporal accesses (each is touched once).
 //
 // Work order: workgroups are dispatched round-robin over the 8 XCDs; the
 // linear tile index is remapped so each XCD receives a contiguous run of
@@ -232,8 +233,8 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
           const int64_t ra = lane_row_atom + 2 * pm, ca = lane_col_atom + 4 * qn + q;
           const int64_t ma = ra < p.M_rep ? ra : p.M_rep - 1;
           const int64_t na = ca < p.N_rep ? ca : p.N_rep - 1;
-          const f32x4 v = load16f(p.C + (((tc.b * p.M_rep + ma) * p.N_rep + na) * 16 +
-                                         (lane & 15)) * 8 + 4 * (lane >> 5));
+          const f32x4 v = load16f_nt(p.C + (((tc.b * p.M_rep + ma) * p.N_rep + na) * 16 +
+                                            (lane & 15)) * 8 + 4 * (lane >> 5));
           acc[pm][qn][4 * q + 0] = v[0];
           acc[pm][qn][4 * q + 1] = v[1];
           acc[pm][qn][4 * q + 2] = v[2];
@@ -299,15 +300,9 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
     issue(cur, s + kStages);
     read_frags(nxt, bn, an);
     mfma_katom(bc[1], ac[1]);
-    // order after the barrier: the next slab's fragment reads first, then
-    // the MFMAs with the loads of slab s+4 spread among them
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (kWaveBlocksM + kWaveBlocksN), 0);
-#pragma unroll
-    for (int i = 0; i < kLoadsPerSlab; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, kWaveBlocksM * kWaveBlocksN - kLoadsPerSlab, 0);
+    // The compiler interleaves these: the MFMAs of the second K half go
+    // first, so the pipe has work right after the barrier, with the loads of
+    // slab s+4 and the next slab's fragment reads spread among them.
   };
   const int64_t n_slabs = (kcn + 3) / 4;
   for (int64_t s = 0; s < n_slabs; s += kStages) {
@@ -334,13 +329,13 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
         if constexpr (kScaled) {
           f32x4 cv = {p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
           if constexpr (kHasC) {
-            if (ok) cv = load16f(p.C + (dst - Dout));
+            if (ok) cv = load16f_nt(p.C + (dst - Dout));
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.alpha, v[e], p.beta * cv[e]);
         }
         if (ok)
-          store16f(dst, v);
+          store16f_nt(dst, v);
       }
 }
 
