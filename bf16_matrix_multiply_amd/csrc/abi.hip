@@ -24,15 +24,32 @@ int hip_status(hipError_t e, const char* what) {
   return BMM_EHIP;
 }
 
+// Launch-grid limits of the kernels (one workgroup per 256 x 256 tile; the
+// skinny kernel's grid is (N/64, M groups, batch); the direct kernel has one
+// wave per 16 x 16 block, four per workgroup).
+bool tiled_fits(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K) {
+  return K < bmm::kTiledMaxK && batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32) <= 0x7fffffff;
+}
+bool skinny_fits(int64_t batch, int64_t M_rep, int64_t N_rep) {
+  return batch <= 65535 && (M_rep + 3) / 4 <= 65535 && (N_rep + 7) / 8 <= 0x7fffffff;
+}
+bool direct_fits(int64_t batch, int64_t M_rep, int64_t N_rep) {
+  return (batch * M_rep * ((N_rep + 1) / 2) + 3) / 4 <= 0x7fffffff;
+}
+
 // Shape rule of BMM_KERNEL_AUTO (K counted in values): the LDS-staged kernel
 // once there are enough 256 x 256 macro tiles to occupy the 256 CUs; the
 // B-streaming kernel when D has at most 64 rows and B is large (at least 16 MB
-// per batch); otherwise one wave per 16 x 16 block.
+// per batch); otherwise one wave per 16 x 16 block. A kernel whose launch
+// grid the shape would overflow is passed over.
 int choose_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K) {
   const int64_t macro_tiles = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
-  if (macro_tiles >= 128 && K < bmm::kTiledMaxK) return BMM_KERNEL_TILED;
-  if (M_rep <= 4 && N_rep * K >= 16 * 65536) return BMM_KERNEL_SKINNY;
-  return BMM_KERNEL_DIRECT;
+  if (macro_tiles >= 128 && tiled_fits(batch, M_rep, N_rep, K)) return BMM_KERNEL_TILED;
+  if (M_rep <= 4 && N_rep * K >= 16 * 65536 && skinny_fits(batch, M_rep, N_rep))
+    return BMM_KERNEL_SKINNY;
+  if (direct_fits(batch, M_rep, N_rep)) return BMM_KERNEL_DIRECT;
+  if (tiled_fits(batch, M_rep, N_rep, K)) return BMM_KERNEL_TILED;
+  return BMM_KERNEL_DIRECT;  // rejected below with a message
 }
 
 // Repeats t < u touch disjoint global boxes when some dimension steps by at
@@ -144,14 +161,28 @@ int mma_common(const bmm::MmaArgs& a0, int32_t kernel, void* stream) {
   if (kernel == BMM_KERNEL_AUTO) kernel = choose_kernel(a0.batch, a0.M_rep, a0.N_rep, K);
   hipStream_t s = static_cast<hipStream_t>(stream);
   switch (kernel) {
-    case BMM_KERNEL_DIRECT: return hip_status(bmm::launch_mma_direct(a0, s), "mma_tile direct launch");
+    case BMM_KERNEL_DIRECT:
+      if (!direct_fits(a0.batch, a0.M_rep, a0.N_rep)) {
+        g_last_error = "mma_tile: too many 16 x 16 blocks for one direct-kernel launch";
+        return BMM_EINVAL;
+      }
+      return hip_status(bmm::launch_mma_direct(a0, s), "mma_tile direct launch");
     case BMM_KERNEL_TILED:
       if (K >= bmm::kTiledMaxK) {
         g_last_error = "mma_tile: the tiled kernel takes K < 4194304 values";
         return BMM_EINVAL;
       }
+      if (!tiled_fits(a0.batch, a0.M_rep, a0.N_rep, K)) {
+        g_last_error = "mma_tile: too many 256 x 256 tiles for one tiled-kernel launch";
+        return BMM_EINVAL;
+      }
       return hip_status(bmm::launch_mma_tiled(a0, s), "mma_tile tiled launch");
-    default: return hip_status(bmm::launch_mma_skinny(a0, s), "mma_tile skinny launch");
+    default:
+      if (!skinny_fits(a0.batch, a0.M_rep, a0.N_rep)) {
+        g_last_error = "mma_tile: the skinny kernel takes batch <= 65535 and M_rep <= 262140";
+        return BMM_EINVAL;
+      }
+      return hip_status(bmm::launch_mma_skinny(a0, s), "mma_tile skinny launch");
   }
 }
 
@@ -221,6 +252,10 @@ int bmm_mma_tile_splitk(float* D, const uint32_t* A, const uint32_t* B, const fl
                                      splits, workspace, workspace_bytes);
   if (!st.ok()) return report(st);
   if (batch == 0 || M_rep == 0 || N_rep == 0) return report(st);
+  if (!tiled_fits(batch, M_rep, N_rep, K_rep * atom_k)) {
+    g_last_error = "mma_tile_splitk: too many 256 x 256 tiles for one launch";
+    return BMM_EINVAL;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t S = bmm::splitk_effective(K_rep, atom_k, splits);
   const int64_t d_floats = batch * M_rep * N_rep * 128;

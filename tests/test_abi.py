@@ -322,3 +322,12 @@ def test_splitk_workspace_and_default(L):
     assert L.bmm_splitk_default(1, 1, 1, 10, 16) == 1
     # empty problems need no workspace and launch nothing
     assert splitk(L, D=0, A=0, B=0, M=0, ws=0, ws_bytes=0) == 0
+
+
+def test_kernel_grid_limits(L):
+    # AUTO passes over a kernel whose grid the shape would overflow: a skinny
+    # shape with more than 65535 batches goes to another kernel
+    assert L.bmm_select_kernel(1, 4, 2048, 1024) == 3
+    assert L.bmm_select_kernel(70000, 4, 2048, 1024) != 3
+    # forcing a kernel past its grid limit is a clear EINVAL, nothing launched
+    assert mma(L, batch=70000, M=1, N=1, K=1, kernel=3) == EINVAL and "skinny" in err(L)
