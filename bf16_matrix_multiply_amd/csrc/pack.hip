@@ -18,6 +18,8 @@ namespace {
 
 constexpr int kPackThreads = 256;
 constexpr int kPackUnroll = 4;
+// The 16-row chunk order below is a permutation of 4 waves x 4 iterations x 64 lanes.
+static_assert(kPackThreads == 256 && kPackUnroll == 4, "chunk order assumes 1024 chunks per block");
 
 template <int R, int KA>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(uint32_t* __restrict__ dst,
@@ -28,11 +30,35 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(uint32_t* __restrict
   const int64_t rb = rb0 + blockIdx.y;
   const uint16_t* srow = src + rb * R * ld;
   uint32_t* drb = dst + rb * int64_t(chunks_per_rb) * 4;
-  const int32_t c0 = blockIdx.x * (kPackThreads * kPackUnroll) + threadIdx.x;
+  // Chunks of this block: a permutation of [base, base + 1024). With 8-row
+  // atoms consecutive lanes take consecutive chunks, so one wave reads 8 rows
+  // x 128 contiguous bytes and writes contiguous 16-byte chunks. With 16-row
+  // atoms that order would read 16 rows x 64 bytes per instruction; instead a
+  // wave takes 8 rows x 4 atoms x 2 halves (k = 16) or 8 rows x 8 atoms
+  // (k = 8), and the other 8 rows come from the unrolled iterations.
+  const int32_t base = blockIdx.x * (kPackThreads * kPackUnroll);
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int32_t cs[kPackUnroll];
+#pragma unroll
+  for (int u = 0; u < kPackUnroll; ++u) {
+    int32_t c_local;
+    if (R == 8) {
+      c_local = threadIdx.x + u * kPackThreads;
+    } else if (KA == 16) {  // c = (kr * 16 + i) * 2 + h
+      const int h = l & 1, i = ((l >> 1) & 7) | ((u & 1) << 3);
+      const int kr = ((l >> 4) & 3) | ((u >> 1) << 2) | (w << 3);
+      c_local = (kr * 16 + i) * 2 + h;
+    } else {  // c = kr * 16 + i
+      const int i = (l & 7) | ((u & 1) << 3);
+      const int kr = ((l >> 3) & 7) | ((u >> 1) << 3) | (w << 4);
+      c_local = kr * 16 + i;
+    }
+    cs[u] = base + c_local;
+  }
   u32x4 v[kPackUnroll];
 #pragma unroll
   for (int u = 0; u < kPackUnroll; ++u) {
-    const int32_t c = c0 + u * kPackThreads;
+    const int32_t c = cs[u];
     if (c < chunks_per_rb) {
       // chunk c: K atom, row in atom, half (k = 16) or K atom, row (k = 8)
       const int32_t i = KA == 16 ? (c >> 1) & (R - 1) : c & (R - 1);
@@ -42,7 +68,7 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(uint32_t* __restrict
   }
 #pragma unroll
   for (int u = 0; u < kPackUnroll; ++u) {
-    const int32_t c = c0 + u * kPackThreads;
+    const int32_t c = cs[u];
     if (c < chunks_per_rb)
       __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(drb + int64_t(c) * 4));
   }

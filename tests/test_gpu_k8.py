@@ -44,7 +44,8 @@ def run_k8(w, inp, kernel, alpha=None, beta=None):
     return A, B, D.cpu().numpy()
 
 
-@pytest.mark.parametrize("shape", [(1, 16, 8, 16), (2, 48, 40, 24), (1, 16, 104, 8)])
+@pytest.mark.parametrize("shape", [(1, 16, 8, 16), (2, 48, 40, 24), (1, 16, 104, 8),
+                                   (1, 32, 16, 1032)])
 def test_pack_k8_bits(shape):
     """Packed words equal the oracle's k = 8 packer, for A (R = 16) and B (R = 8),
     with a row pitch wider than K."""

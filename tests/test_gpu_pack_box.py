@@ -23,7 +23,8 @@ def test_pack_all_bit_patterns(R):
 
 
 @pytest.mark.parametrize("R,rows,K,ld", [(16, 16, 16, 16), (8, 8, 32, 40), (16, 48, 80, 96),
-                                         (8, 40, 2064, 2072), (16, 272, 336, 336)])
+                                         (8, 40, 2064, 2072), (16, 272, 336, 336),
+                                         (16, 32, 1040, 1048)])
 def test_pack_shapes_and_row_padding(R, rows, K, ld):
     rng = np.random.default_rng(rows + K)
     x = util.random_bits(rng, (3, rows, ld))
