@@ -37,16 +37,20 @@ bool direct_fits(int64_t batch, int64_t M_rep, int64_t N_rep) {
   return (batch * M_rep * ((N_rep + 1) / 2) + 3) / 4 <= 0x7fffffff;
 }
 
-// Shape rule of BMM_KERNEL_AUTO (K counted in values): the LDS-staged kernel
-// once there are enough 256 x 256 macro tiles to occupy the 256 CUs; the
-// B-streaming kernel when D has at most 64 rows and B is large (at least 16 MB
-// per batch); otherwise one wave per 16 x 16 block. A kernel whose launch
-// grid the shape would overflow is passed over.
+// Shape rule of BMM_KERNEL_AUTO (K counted in values), from a sweep of the
+// three kernels over shapes from 16 x 1024 x 1024 to 4096^3 on MI355X:
+// - the LDS-staged kernel when its 256 x 256 tiles are full in both
+//   directions and there are at least 48 of them (2048^3, 64 tiles: 44 us
+//   against 51 us for the next best);
+// - otherwise the K-splitting, B-streaming kernel, which was the fastest or
+//   tied for every shape with fewer or partial tiles (1024 x 1024 x 8192:
+//   41 us against 66 us direct; 256 x 4096 x 4096: 23 against 34 us);
+// - the direct kernel where the others' launch grids would overflow.
 int choose_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K) {
   const int64_t macro_tiles = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
-  if (macro_tiles >= 128 && tiled_fits(batch, M_rep, N_rep, K)) return BMM_KERNEL_TILED;
-  if (M_rep <= 4 && N_rep * K >= 16 * 65536 && skinny_fits(batch, M_rep, N_rep))
-    return BMM_KERNEL_SKINNY;
+  if (M_rep >= 16 && N_rep >= 32 && macro_tiles >= 48 && tiled_fits(batch, M_rep, N_rep, K))
+    return BMM_KERNEL_TILED;
+  if (skinny_fits(batch, M_rep, N_rep)) return BMM_KERNEL_SKINNY;
   if (direct_fits(batch, M_rep, N_rep)) return BMM_KERNEL_DIRECT;
   if (tiled_fits(batch, M_rep, N_rep, K)) return BMM_KERNEL_TILED;
   return BMM_KERNEL_DIRECT;  // rejected below with a message
@@ -234,12 +238,19 @@ int bmm_splitk_default(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_re
       (atom_k != 16 && atom_k != 8))
     return BMM_EINVAL;
   // Enough 256 x 256 tiles x splits to give every CU a workgroup, with each
-  // split at least 64 steps (2048 K values) deep so that its partial-sum
-  // traffic stays small against its MFMA time.
+  // split at least 32 steps (1024 K values) deep so that its partial-sum
+  // traffic stays small against its MFMA time (measured best or within 10%
+  // of best at 2048^3, 1024 x 1024 x 8192, 2048 x 2048 x 8192 and
+  // 512 x 512 x 65536).
   const int64_t tiles = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
   const int64_t steps = (K_rep * atom_k + 31) / 32;
-  int64_t s = tiles > 0 ? (256 + tiles - 1) / tiles : 1;
-  if (s > steps / 64) s = steps / 64;
+  // (rounded down: 144 tiles stay whole, as two splits would leave a second
+  // partial wave of workgroups)
+  int64_t s = tiles > 0 ? 256 / tiles : 1;
+  if (s > steps / 32) s = steps / 32;
+  // at most 32 partial sums: at 512 x 512 x 65536, 32 splits took 66 us and
+  // 64 splits 82 us (the reduce reads every partial once)
+  if (s > 32) s = 32;
   if (s > 65535) s = 65535;
   return int(s < 1 ? 1 : s);
 }

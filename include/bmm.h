@@ -43,13 +43,15 @@ enum {
   BMM_EHIP = -5      /* the HIP runtime reported an error at launch */
 };
 
-/* Kernel selection for bmm_mma_tile_with. AUTO picks by shape; the others
- * force one kernel (every kernel accepts every valid shape). */
+/* Kernel selection for bmm_mma_tile_with. AUTO picks by shape (TILED when
+ * there are at least 48 full 256 x 256 tiles, else SKINNY, else DIRECT if a
+ * grid limit rules SKINNY out); the others force one kernel (every kernel
+ * accepts every valid shape within its launch-grid limits). */
 typedef enum {
   BMM_KERNEL_AUTO = 0,
   BMM_KERNEL_DIRECT = 1, /* one wave per 16x16 output block, operands straight from HBM */
   BMM_KERNEL_TILED = 2,  /* LDS-staged 256x256 macro tiles for large M and N */
-  BMM_KERNEL_SKINNY = 3  /* small M: split-K across waves, B streamed once */
+  BMM_KERNEL_SKINNY = 3  /* few output tiles: K split across the waves of a workgroup, B streamed */
 } bmm_kernel;
 
 /*
@@ -331,7 +333,7 @@ int64_t bmm_mma_splitk_workspace_bytes(int64_t batch, int64_t M_rep, int64_t N_r
                                        int64_t K_rep, int32_t atom_k, int32_t splits);
 
 /* A split count for bmm_mma_tile_splitk: enough tiles x splits for every CU,
- * each split at least 2048 K values deep; 1 when splitting does not pay. */
+ * each split at least 1024 K values deep; 1 when splitting does not pay. */
 int bmm_splitk_default(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep,
                        int32_t atom_k);
 
