@@ -16,10 +16,7 @@ enum : int { kF16 = 0, kBF16 = 1 };
 
 constexpr int kWave = 64;
 
-// Words per packed atom: A atom 16 rows x 8 words, B atom 8 rows x 8 words,
-// accumulator atom 16 x 8 floats.
-constexpr int kAtomWordsA = 128;
-constexpr int kAtomWordsB = 64;
+// Floats per accumulator atom (16 rows x 8 columns).
 constexpr int kAtomFloats = 128;
 
 // One v_mfma_f32_16x16x32_{f16,bf16}: acc[i][j] += sum_k x[i][k] * y[k][j].

@@ -13,33 +13,36 @@
 //
 // Fragment map (B fed as the first operand, A as the second, so the result is
 // D transposed): lane l supplies row n = l % 32 of a 32-column block of B and
-// row m = l % 32 of a 32-row block of A, each with the 8 K values of half
-// l / 32 of one K atom (16 K values per operation). It receives 16 floats:
+// row m = l % 32 of a 32-row block of A, each with the 8 K values of chunk
+// l / 32 of the operation's 16 (half of one k = 16 atom, or one whole k = 8
+// atom). It receives 16 floats:
 // register r = 4q + t holds D[m = l % 32][n = 8q + 4 * (l / 32) + t], i.e.
 // for each q one contiguous 16-byte piece of N atom q of the block.
 //
 // Macro tile 256 (M) x 256 (N), 8 waves (two per SIMD) in a 2 x 4 grid, each
 // wave owning a 128 x 64 block of D = 4 x 2 blocks of 32 x 32 (8 accumulators
-// of 16 floats per lane, held in AGPRs). The two waves of a SIMD run the same
+// of 16 floats per lane, 128 registers). The two waves of a SIMD run the same
 // pipeline, so while one waits on a load or a barrier the other issues MFMAs.
-// K advances in slabs of 32 (2 K atoms).
+// K advances in slabs of 32 values (four 8-value chunks: 2 atoms of k = 16 or
+// 4 of k = 8).
 //
 // Staging takes the role the pages give to TMA box loads ("cp.async.bulk.
 // tensor" page). The LDS image of a slab is fragment-major: 16 A fragments
-// (8 row blocks x 2 K atoms) and 16 B fragments of 1 KB each, every fragment
+// (8 row blocks x 2 K halves) and 16 B fragments of 1 KB each, every fragment
 // stored in lane order, so one direct-to-LDS buffer load (each lane's 16
 // bytes land at M0 + 16 * lane) writes exactly one fragment, gathered from
 // two A atoms or four B atoms in HBM, and one ds_read_b128 per lane reads it
 // back contiguously (no bank conflicts). Loads run four slabs deep: a ring of
 // four 32 KB stages, with slab s+4 loaded into the stage slab s has just left.
-// Rows past M_rep / N_rep and K atoms past K_rep read as zero through the
-// buffer range check, so the loop has no branches; slabs past the end load as
-// zeros and are multiplied harmlessly.
+// Rows past M_rep / N_rep read as zero through the buffer range check and K
+// chunks past the end are given an out-of-range offset, so the loop has no
+// branches; slabs past the end load as zeros and are multiplied harmlessly.
+// A second grid axis, when present, splits K (split-K form, below).
 //
-// Per slab each wave: the MFMAs of the first K atom on fragments already in
-// registers; wait for its own loads of the next slab and its fragment reads;
-// barrier; issue the loads of slab s+4; read the next slab's fragments; the
-// MFMAs of the second K atom. The barrier is a bare s_barrier after a counted
+// Per slab each wave: the MFMAs of the first 16-value half on fragments already
+// in registers; wait for its own loads of the next slab and its fragment
+// reads; barrier; issue the loads of slab s+4; read the next slab's fragments;
+// the MFMAs of the second half. The barrier is a bare s_barrier after a counted
 // wait, so the loads of later slabs stay in flight across it. C is read and D
 // written with non-temporal accesses (each is touched once).
 //
@@ -61,9 +64,8 @@ constexpr int kWaveBlocksM = 4;   // 32-row blocks per wave
 constexpr int kWaveBlocksN = 2;   // 32-column blocks per wave
 constexpr int kTileMAtoms = 16;   // 256 rows
 constexpr int kTileNAtoms = 32;   // 256 columns
-constexpr int kSlabKAtoms = 2;    // 32 K values
-constexpr int kFragsA = 16;       // per slab: 8 blocks of 32 rows x 2 K atoms
-constexpr int kFragsB = 16;       // per slab: 8 blocks of 32 columns x 2 K atoms
+constexpr int kFragsA = 16;       // per slab: 8 blocks of 32 rows x 2 K halves
+constexpr int kFragsB = 16;       // per slab: 8 blocks of 32 columns x 2 K halves
 constexpr int kLoadsA = kFragsA / kWaves;                 // per wave and slab, one fragment each
 constexpr int kLoadsB = kFragsB / kWaves;
 constexpr int kLoadsPerSlab = kLoadsA + kLoadsB;
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
 
-  // Fragments of one slab: [K atom][block]. Reads are volatile LDS loads so
+  // Fragments of one slab: [K half][block]. Reads are volatile LDS loads so
   // they stay where they are written (a half slab ahead of their MFMAs)
   // instead of being sunk to their first use.
   using FragB = u32x4[2][kWaveBlocksN];

@@ -7,9 +7,9 @@
 // this little-endian machine), so packing is a permutation of 16-byte chunks:
 // output chunk (row block rb, c) with c = (kr, i, h) comes from source row
 // R*rb + i, K offset 16*kr + 8*h (with an atom K of 8: c = (kr, i), K offset
-// 8*kr). Stores are fully contiguous; each 32-byte
-// piece of a source row is read by two adjacent lanes, and the K atoms of one
-// row are read by the same block in successive chunk groups.
+// 8*kr). A block takes 1024 consecutive output chunks; the order in which its
+// lanes take them (below) keeps both the row reads and the chunk writes in
+// runs of 128 bytes or more.
 #include "common.h"
 #include "launch.h"
 

@@ -24,6 +24,7 @@ import csv
 import hashlib
 import json
 import os
+import re
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -35,12 +36,21 @@ KERNEL_SOURCES = {
 KERNEL_MATCH = {"mma_tile": "mma_", "pack_operand": "pack_kernel"}
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and with whitespace collapsed, so that a
+    comment edit does not mark counter records stale (the kernels' sources
+    hold no string literal containing a comment marker)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_sha(kernel: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
         p = os.path.join(ROOT, "bf16_matrix_multiply_amd", "csrc", f)
         if os.path.exists(p):
-            h.update(open(p, "rb").read())
+            h.update(_code_only(open(p).read()).encode())
     return h.hexdigest()[:16]
 
 
