@@ -107,7 +107,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=workloads.HEADLINE,
                     choices=sorted(workloads.WORKLOADS) + sorted(workloads.EXTRA_WORKLOADS))
-    ap.add_argument("--kernel", default="auto", choices=["auto", "direct", "tiled", "skinny"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "direct", "tiled", "skinny", "tiled128"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--alpha", type=float, default=None,

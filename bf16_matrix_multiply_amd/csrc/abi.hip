@@ -27,8 +27,9 @@ int hip_status(hipError_t e, const char* what) {
 // Launch-grid limits of the kernels (one workgroup per 256 x 256 tile; the
 // skinny kernel's grid is (N/64, M groups, batch); the direct kernel has one
 // wave per 16 x 16 block, four per workgroup).
-bool tiled_fits(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K) {
-  return K < bmm::kTiledMaxK && batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32) <= 0x7fffffff;
+bool tiled_fits(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K, int tile = 256) {
+  const int64_t ma = tile / 16, na = tile / 8;  // M and N atoms per tile
+  return K < bmm::kTiledMaxK && batch * ((M_rep + ma - 1) / ma) * ((N_rep + na - 1) / na) <= 0x7fffffff;
 }
 bool skinny_fits(int64_t batch, int64_t M_rep, int64_t N_rep) {
   return batch <= 65535 && (M_rep + 3) / 4 <= 65535 && (N_rep + 7) / 8 <= 0x7fffffff;
@@ -38,21 +39,27 @@ bool direct_fits(int64_t batch, int64_t M_rep, int64_t N_rep) {
 }
 
 // Shape rule of BMM_KERNEL_AUTO (K counted in values), from a sweep of the
-// three kernels over shapes from 16 x 1024 x 1024 to 4096^3 on MI355X:
-// - the LDS-staged kernel when its 256 x 256 tiles are full in both
-//   directions and there are at least 48 of them (2048^3, 64 tiles: 44 us
-//   against 51 us for the next best);
-// - otherwise the K-splitting, B-streaming kernel, which was the fastest or
-//   tied for every shape with fewer or partial tiles (1024 x 1024 x 8192:
-//   41 us against 66 us direct; 256 x 4096 x 4096: 23 against 34 us);
+// kernels over shapes from 16 x 1024 x 1024 to 8192^3 on MI355X:
+// - 256 x 256 LDS tiles when there are at least 128 full ones (3072^3, 144
+//   tiles: 66 us against 69 us with 128 x 128 tiles; 2560^3, 100 tiles, is
+//   faster with the smaller tile);
+// - 128 x 128 LDS tiles when there are at least 128 full ones (2048^3: 24 us
+//   against 42 us with the large tile; 1536^3: 17 against 31 us for the next
+//   best);
+// - otherwise the K-splitting, B-streaming kernel, fastest or tied for every
+//   shape with fewer tiles (1024 x 1024 x 8192: 39 against 58 us;
+//   256 x 4096 x 4096: 24 against 32 us);
 // - the direct kernel where the others' launch grids would overflow.
 int choose_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K) {
-  const int64_t macro_tiles = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
-  if (M_rep >= 16 && N_rep >= 32 && macro_tiles >= 48 && tiled_fits(batch, M_rep, N_rep, K))
+  const int64_t tiles256 = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
+  const int64_t tiles128 = batch * ((M_rep + 7) / 8) * ((N_rep + 15) / 16);
+  if (M_rep >= 16 && N_rep >= 32 && tiles256 >= 128 && tiled_fits(batch, M_rep, N_rep, K))
     return BMM_KERNEL_TILED;
+  if (M_rep >= 8 && N_rep >= 16 && tiles128 >= 128 && tiled_fits(batch, M_rep, N_rep, K, 128))
+    return BMM_KERNEL_TILED_128;
   if (skinny_fits(batch, M_rep, N_rep)) return BMM_KERNEL_SKINNY;
   if (direct_fits(batch, M_rep, N_rep)) return BMM_KERNEL_DIRECT;
-  if (tiled_fits(batch, M_rep, N_rep, K)) return BMM_KERNEL_TILED;
+  if (tiled_fits(batch, M_rep, N_rep, K, 128)) return BMM_KERNEL_TILED_128;
   return BMM_KERNEL_DIRECT;  // rejected below with a message
 }
 
@@ -172,15 +179,20 @@ int mma_common(const bmm::MmaArgs& a0, int32_t kernel, void* stream) {
       }
       return hip_status(bmm::launch_mma_direct(a0, s), "mma_tile direct launch");
     case BMM_KERNEL_TILED:
+    case BMM_KERNEL_TILED_128: {
+      const int tile = kernel == BMM_KERNEL_TILED ? 256 : 128;
       if (K >= bmm::kTiledMaxK) {
         g_last_error = "mma_tile: the tiled kernel takes K < 4194304 values";
         return BMM_EINVAL;
       }
-      if (!tiled_fits(a0.batch, a0.M_rep, a0.N_rep, K)) {
-        g_last_error = "mma_tile: too many 256 x 256 tiles for one tiled-kernel launch";
+      if (!tiled_fits(a0.batch, a0.M_rep, a0.N_rep, K, tile)) {
+        g_last_error = "mma_tile: too many macro tiles for one tiled-kernel launch";
         return BMM_EINVAL;
       }
-      return hip_status(bmm::launch_mma_tiled(a0, s), "mma_tile tiled launch");
+      bmm::MmaArgs a = a0;
+      a.tile = tile;
+      return hip_status(bmm::launch_mma_tiled(a, s), "mma_tile tiled launch");
+    }
     default:
       if (!skinny_fits(a0.batch, a0.M_rep, a0.N_rep)) {
         g_last_error = "mma_tile: the skinny kernel takes batch <= 65535 and M_rep <= 262140";

@@ -26,6 +26,8 @@ struct MmaArgs {
   // into that many ranges, partial sums from zero to D + s * part_floats
   int splits;
   int64_t steps, part_floats;
+  // tiled kernel macro tile: 256 (default, also for 0) or 128
+  int tile;
 };
 
 // In 8-value K chunks, one 32-deep MFMA step spans the same bytes in either

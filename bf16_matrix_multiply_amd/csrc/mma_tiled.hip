@@ -58,16 +58,24 @@
 namespace bmm {
 namespace {
 
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * kWave;
-constexpr int kWaveBlocksM = 4;   // 32-row blocks per wave
-constexpr int kWaveBlocksN = 2;   // 32-column blocks per wave
-constexpr int kTileMAtoms = 16;   // 256 rows
-constexpr int kTileNAtoms = 32;   // 256 columns
-constexpr int kFragsA = 16;       // per slab: 8 blocks of 32 rows x 2 K halves
-constexpr int kFragsB = 16;       // per slab: 8 blocks of 32 columns x 2 K halves
-constexpr int kLoadsA = kFragsA / kWaves;                 // per wave and slab, one fragment each
-constexpr int kLoadsB = kFragsB / kWaves;
+// Macro tile shapes. TM = 256: 8 waves (two per SIMD) in a 2 x 4 grid, each
+// 128 x 64 of D, one workgroup per CU. TM = 128, for problems with too few
+// 256 x 256 tiles to occupy the chip: 4 waves in a 2 x 2 grid, each 64 x 64,
+// a 64 KB ring, two workgroups per CU.
+template <int TM>
+struct Tile {
+  static constexpr int kWaves = TM == 256 ? 8 : 4;
+  static constexpr int kWavesN = TM == 256 ? 4 : 2;     // wave grid columns
+  static constexpr int kWaveBlocksM = TM == 256 ? 4 : 2;  // 32-row blocks per wave
+  static constexpr int kWaveBlocksN = 2;                  // 32-column blocks per wave
+  static constexpr int kTileMAtoms = TM / 16;
+  static constexpr int kTileNAtoms = TM / 8;
+  static constexpr int kFragsA = TM / 16;   // per slab: TM/32 blocks of 32 rows x 2 K halves
+  static constexpr int kFragsB = TM / 16;   // per slab: TM/32 blocks of 32 columns x 2 K halves
+};
+// Both shapes give every wave one A and one B fragment per 16-value half of a
+// slab: two loads of each operand per slab.
+constexpr int kLoadsA = 2, kLoadsB = 2;
 constexpr int kLoadsPerSlab = kLoadsA + kLoadsB;
 constexpr int kStages = 4;
 constexpr int kXcds = 8;
@@ -85,9 +93,10 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
 constexpr int kWaitVmcnt0 = waitcnt_imm(0, 15);
 
 // One ring stage: fragment f of each operand is 64 lanes x 16 bytes.
+template <int TM>
 struct Stage {
-  u32x4 a[kFragsA][kWave];
-  u32x4 b[kFragsB][kWave];
+  u32x4 a[Tile<TM>::kFragsA][kWave];
+  u32x4 b[Tile<TM>::kFragsB][kWave];
 };
 
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -127,16 +136,23 @@ __device__ __forceinline__ TileCoord tile_of(int64_t w, int64_t n_tiles, int64_t
   return c;
 }
 
-template <int DT, int KA, bool kHasC, bool kScaled>
-__global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64_t n_tiles,
-                                                               int64_t MT, int64_t NT) {
+template <int TM, int DT, int KA, bool kHasC, bool kScaled>
+__global__ __launch_bounds__(Tile<TM>::kWaves * kWave)
+__attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t n_tiles,
+                                                              int64_t MT, int64_t NT) {
+  using T = Tile<TM>;
+  using Stage = bmm::Stage<TM>;
+  constexpr int kWaves = T::kWaves, kWaveBlocksM = T::kWaveBlocksM, kWaveBlocksN = T::kWaveBlocksN;
+  constexpr int kTileMAtoms = T::kTileMAtoms, kTileNAtoms = T::kTileNAtoms;
+  static_assert(T::kFragsA == kLoadsA * kWaves && T::kFragsB == kLoadsB * kWaves,
+                "one load per fragment");
   // Four separate objects (not one array) so that the compiler can tell the
   // ring slots apart when it places waits for the direct-to-LDS loads.
   __shared__ __attribute__((aligned(1024))) Stage st0, st1, st2, st3;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / T::kWavesN, wn = wave % T::kWavesN;
   const TileCoord tc = tile_of(blockIdx.x, n_tiles, MT, NT);
   const int64_t m_atom0 = tc.mt * kTileMAtoms, n_atom0 = tc.nt * kTileNAtoms;
 
@@ -341,20 +357,20 @@ __global__ __launch_bounds__(kThreads, 1) void mma_tiled_kernel(MmaArgs p, int64
       }
 }
 
-}  // namespace
-
-hipError_t launch_mma_tiled(const MmaArgs& a, hipStream_t s) {
+template <int TM>
+hipError_t launch_tm(const MmaArgs& a, hipStream_t s) {
+  constexpr int kTileMAtoms = Tile<TM>::kTileMAtoms, kTileNAtoms = Tile<TM>::kTileNAtoms;
   const int64_t MT = (a.M_rep + kTileMAtoms - 1) / kTileMAtoms;
   const int64_t NT = (a.N_rep + kTileNAtoms - 1) / kTileNAtoms;
   const int64_t n_tiles = a.batch * MT * NT;
   if (n_tiles > 0x7fffffff) return hipErrorInvalidConfiguration;
-  // Buffer offsets inside one tile's 16 A atom rows must stay below 2^31.
+  // Buffer offsets inside one tile's atom rows must stay below 2^31.
   if (k_chunks(a) * 8 >= kTiledMaxK) return hipErrorInvalidValue;
   auto pick = [&](auto dt, auto ka) {
     constexpr int D = decltype(dt)::value, KA = decltype(ka)::value;
     if (a.scaled)
-      return a.C ? mma_tiled_kernel<D, KA, true, true> : mma_tiled_kernel<D, KA, false, true>;
-    return a.C ? mma_tiled_kernel<D, KA, true, false> : mma_tiled_kernel<D, KA, false, false>;
+      return a.C ? mma_tiled_kernel<TM, D, KA, true, true> : mma_tiled_kernel<TM, D, KA, false, true>;
+    return a.C ? mma_tiled_kernel<TM, D, KA, true, false> : mma_tiled_kernel<TM, D, KA, false, false>;
   };
   auto pick_ka = [&](auto dt) {
     return a.atom_k == 16 ? pick(dt, std::integral_constant<int, 16>{})
@@ -363,9 +379,15 @@ hipError_t launch_mma_tiled(const MmaArgs& a, hipStream_t s) {
   auto kern = a.dtype == kBF16 ? pick_ka(std::integral_constant<int, kBF16>{})
                                : pick_ka(std::integral_constant<int, kF16>{});
   const unsigned splits = a.splits > 1 ? unsigned(a.splits) : 1u;
-  hipLaunchKernelGGL(kern, dim3(unsigned(n_tiles), splits), dim3(kThreads), 0, s, a, n_tiles, MT,
-                     NT);
+  hipLaunchKernelGGL(kern, dim3(unsigned(n_tiles), splits), dim3(Tile<TM>::kWaves * kWave), 0, s,
+                     a, n_tiles, MT, NT);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mma_tiled(const MmaArgs& a, hipStream_t s) {
+  return a.tile == 128 ? launch_tm<128>(a, s) : launch_tm<256>(a, s);
 }
 
 }  // namespace bmm

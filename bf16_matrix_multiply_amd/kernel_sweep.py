@@ -16,11 +16,12 @@ import torch
 
 import bf16_matrix_multiply_amd as bmm
 
-DEFAULT_SHAPES = [(128, 128, 256), (512, 512, 512), (1024, 1024, 1024), (2048, 2048, 2048),
-                  (3072, 3072, 3072), (4096, 4096, 1024), (4096, 4096, 4096), (8192, 8192, 8192),
-                  (1024, 1024, 8192), (2048, 2048, 8192), (1024, 1024, 65536), (512, 512, 65536),
-                  (16, 1024, 1024), (64, 2048, 2048), (256, 4096, 4096), (64, 8192, 8192),
-                  (32, 16384, 4096), (16, 16384, 16384)]
+DEFAULT_SHAPES = [(128, 128, 256), (512, 512, 512), (1024, 1024, 1024), (1536, 1536, 1536),
+                  (2048, 2048, 2048), (2560, 2560, 2560), (3072, 3072, 3072), (4096, 4096, 1024),
+                  (4096, 4096, 4096), (8192, 8192, 8192), (1024, 1024, 8192), (2048, 2048, 8192),
+                  (1024, 4096, 4096), (2048, 1024, 4096), (1024, 1024, 65536), (512, 512, 65536),
+                  (16, 1024, 1024), (64, 2048, 2048), (256, 4096, 4096), (512, 2048, 2048),
+                  (64, 8192, 8192), (32, 16384, 4096), (16, 16384, 16384)]
 
 
 def _median_us(fn, reps=8):
@@ -45,7 +46,7 @@ def sweep(shapes):
         A, B = bmm.pack_operand(a, 16), bmm.pack_operand(b, 8)
         D = torch.empty(1, M // 16, N // 8, 16, 8, device=dev)
         times = {}
-        for k in ("direct", "tiled", "skinny"):
+        for k in ("direct", "tiled", "tiled128", "skinny"):
             times[k] = _median_us(lambda: bmm.mma_tile(A, B, None, 0.0, "bf16", out=D, kernel=k))
         auto = bmm.select_kernel(1, M // 16, N // 8, K // 16)
         default = bmm.splitk_default(1, M // 16, N // 8, K // 16)

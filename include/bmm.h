@@ -43,15 +43,17 @@ enum {
   BMM_EHIP = -5      /* the HIP runtime reported an error at launch */
 };
 
-/* Kernel selection for bmm_mma_tile_with. AUTO picks by shape (TILED when
- * there are at least 48 full 256 x 256 tiles, else SKINNY, else DIRECT if a
- * grid limit rules SKINNY out); the others force one kernel (every kernel
- * accepts every valid shape within its launch-grid limits). */
+/* Kernel selection for bmm_mma_tile_with. AUTO picks by shape (TILED with at
+ * least 128 full 256 x 256 tiles, else TILED_128 with at least 128 full
+ * 128 x 128 tiles, else SKINNY, else DIRECT if a grid limit rules the others
+ * out); the others force one kernel (every kernel accepts every valid shape
+ * within its launch-grid limits). */
 typedef enum {
   BMM_KERNEL_AUTO = 0,
   BMM_KERNEL_DIRECT = 1, /* one wave per 16x16 output block, operands straight from HBM */
   BMM_KERNEL_TILED = 2,  /* LDS-staged 256x256 macro tiles for large M and N */
-  BMM_KERNEL_SKINNY = 3  /* few output tiles: K split across the waves of a workgroup, B streamed */
+  BMM_KERNEL_SKINNY = 3, /* few output tiles: K split across the waves of a workgroup, B streamed */
+  BMM_KERNEL_TILED_128 = 4 /* LDS-staged 128x128 macro tiles, two workgroups per CU */
 } bmm_kernel;
 
 /*

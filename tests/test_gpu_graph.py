@@ -15,7 +15,8 @@ from tests import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("form", ["plain_tiled", "plain_direct", "splitk", "scaled", "k8"])
+@pytest.mark.parametrize("form", ["plain_tiled", "plain_tiled128", "plain_direct", "splitk", "scaled",
+                                  "k8"])
 def test_graph_replays_match_eager(form):
     w = workloads.custom(1, 528, 520, 1040, "bf16", c_tensor=True)
     inp = workloads.make_inputs(w, seed=6)
@@ -39,6 +40,8 @@ def test_graph_replays_match_eager(form):
             bmm.mma_tile(A, B, C, 0.0, "bf16", out=D, kernel="tiled", alpha=0.5, beta=-1.5)
         elif form == "plain_direct":
             bmm.mma_tile(A, B, C, 0.0, "bf16", out=D, kernel="direct")
+        elif form == "plain_tiled128":
+            bmm.mma_tile(A, B, C, 0.0, "bf16", out=D, kernel="tiled128")
         else:
             bmm.mma_tile(A, B, C, 0.0, "bf16", out=D, kernel="tiled")
 

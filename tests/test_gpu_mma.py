@@ -17,7 +17,7 @@ from tests import util
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = ["direct", "tiled", "skinny"]
+KERNELS = ["direct", "tiled", "skinny", "tiled128"]
 
 C = workloads.custom
 SMALL = {
