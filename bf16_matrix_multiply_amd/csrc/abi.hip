@@ -232,6 +232,20 @@ int bmm_mma_tile_opts(float* D, const uint32_t* A, const uint32_t* B, const floa
   return mma_common(a, o.kernel, stream);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Macro tile of the split-K form: 128 x 128 up to 16384 K values, 256 x 256
+// beyond. Measured best-over-splits (us, 256 / 128 tiles): 1024 x 1024 x 8192
+// 39.8 / 32.1, 64 x 8192 x 8192 37.0 / 29.4, 2048 x 2048 x 16384 134 / 135,
+// 1024 x 1024 x 65536 144 / 172, 512 x 512 x 65536 65 / 69.
+int splitk_tile(int64_t K) { return K <= 16384 ? 128 : 256; }
+
+}  // namespace
+
+extern "C" {
+
 int64_t bmm_mma_splitk_workspace_bytes(int64_t batch, int64_t M_rep, int64_t N_rep,
                                        int64_t K_rep, int32_t atom_k, int32_t splits) {
   if (batch < 0 || M_rep < 0 || N_rep < 0 || K_rep < 0 || K_rep > (int64_t(1) << 26) ||
@@ -249,13 +263,14 @@ int bmm_splitk_default(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_re
   if (batch < 0 || M_rep < 0 || N_rep < 0 || K_rep < 0 || K_rep > (int64_t(1) << 26) ||
       (atom_k != 16 && atom_k != 8))
     return BMM_EINVAL;
-  // Enough 256 x 256 tiles x splits to give every CU a workgroup, with each
-  // split at least 32 steps (1024 K values) deep so that its partial-sum
-  // traffic stays small against its MFMA time (measured best or within 10%
-  // of best at 2048^3, 1024 x 1024 x 8192, 2048 x 2048 x 8192 and
-  // 512 x 512 x 65536).
-  const int64_t tiles = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
+  // Enough tiles x splits (tiles of the size splitk_tile picks) to give every
+  // CU a workgroup, with each split at least 32 steps (1024 K values) deep so
+  // that its partial-sum traffic stays small against its MFMA time (measured
+  // best or within 10% of best at 1024 x 1024 x 8192, 64 x 8192 x 8192,
+  // 2048 x 2048 x 8192, 1024 x 1024 x 65536 and 512 x 512 x 65536).
   const int64_t steps = (K_rep * atom_k + 31) / 32;
+  const int64_t ta = splitk_tile(K_rep * atom_k) / 16, tb = splitk_tile(K_rep * atom_k) / 8;
+  const int64_t tiles = batch * ((M_rep + ta - 1) / ta) * ((N_rep + tb - 1) / tb);
   // (rounded down: 144 tiles stay whole, as two splits would leave a second
   // partial wave of workgroups)
   int64_t s = tiles > 0 ? 256 / tiles : 1;
@@ -275,8 +290,9 @@ int bmm_mma_tile_splitk(float* D, const uint32_t* A, const uint32_t* B, const fl
                                      splits, workspace, workspace_bytes);
   if (!st.ok()) return report(st);
   if (batch == 0 || M_rep == 0 || N_rep == 0) return report(st);
-  if (!tiled_fits(batch, M_rep, N_rep, K_rep * atom_k)) {
-    g_last_error = "mma_tile_splitk: too many 256 x 256 tiles for one launch";
+  const int tile = splitk_tile(K_rep * atom_k);
+  if (!tiled_fits(batch, M_rep, N_rep, K_rep * atom_k, tile)) {
+    g_last_error = "mma_tile_splitk: too many macro tiles for one launch";
     return BMM_EINVAL;
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -289,6 +305,7 @@ int bmm_mma_tile_splitk(float* D, const uint32_t* A, const uint32_t* B, const fl
     a.splits = int(S);
     a.steps = (K_rep * atom_k + 31) / 32;
     a.part_floats = d_floats;
+    a.tile = tile;
     const int rc = hip_status(bmm::launch_mma_tiled(a, s), "mma_tile_splitk tiled launch");
     if (rc != BMM_OK) return rc;
   }
