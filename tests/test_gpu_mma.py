@@ -204,6 +204,26 @@ def test_full_quantised_variants(name):
     gu.assert_parity_sampled(w, inp, D)
 
 
+@pytest.mark.parametrize("shape,kernel", [((2048, 2048, 2048), "auto"),
+                                          ((2560, 1536, 4096), "tiled128"),
+                                          ((4096, 4096, 4096), "tiled128")])
+def test_mid_size_tiled128_sampled(shape, kernel):
+    """Mid-size shapes on the 128 x 128 tile (AUTO's pick at 2048^3): normal
+    bf16 data with a C tensor, sampled outputs within bound, and the same
+    shape with quarter-integer f16 data bit-exact on its samples."""
+    M, N, K = shape
+    if kernel == "auto":
+        assert bmm.select_kernel(1, M // 16, N // 8, K // 16) == "tiled128"
+    w = C(1, M, N, K, "bf16", c_tensor=True, name=f"mid_{M}x{N}x{K}")
+    inp = inputs(w)
+    _, _, _, D = gu.gpu_run(w, inp, kernel)
+    gu.assert_parity_sampled(w, inp, D)
+    wq = C(1, M, N, K, "f16", "quarter", "quarter", c_tensor=True, name=f"mid_q_{M}x{N}x{K}")
+    inpq = workloads.make_inputs(wq, seed=3)
+    _, _, _, Dq = gu.gpu_run(wq, inpq, kernel)
+    gu.assert_parity_sampled(wq, inpq, Dq)
+
+
 # ---- alpha/beta form (bmm_mma_tile_scaled) ----
 
 SCALED = {
