@@ -296,6 +296,8 @@ def main():
         "roofline": roofline,
         "kernels": {"pack_a_us": round(pa.mean() * 1e3, 2), "pack_b_us": round(pb.mean() * 1e3, 2),
                     "mma_tile_us": round(mm.mean() * 1e3, 2),
+                    "mma_tile_median_us": round(float(np.median(mm)) * 1e3, 2),
+                    "mma_tile_min_us": round(float(mm.min()) * 1e3, 2),
                     "mma_tile_tflops": round(w.flops / mma_s / 1e12, 2),
                     "mma_tile_gbs": round(w.algorithmic_bytes / mma_s / 1e9, 1),
                     "pack_gbs": round((op_bytes + op_bytes_b) / ((pa.mean() + pb.mean()) * 1e-3)
