@@ -180,6 +180,7 @@ def pack_km(L, dst=P0, src=P1, batch=1, rows=16, K=32, ld=16, R=16):
     (dict(ld=20), EALIGN, "multiple of 8"),
     (dict(batch=70000), EINVAL, "too large"),
     (dict(K=(1 << 22) + 16), EINVAL, "too large"),
+    (dict(K=1 << 22), EINVAL, "too large"),         # K / 64 would exceed the grid's y limit
     (dict(dst=P0 + 4), EALIGN, "aligned"),
     (dict(dst=0), EINVAL, "null"),
     (dict(dst=P1 + 32), EOVERLAP, "overlaps"),
