@@ -80,8 +80,9 @@ Status check_pack_kmajor(const uint32_t* dst, const uint16_t* src, int64_t batch
   if (batch < 0 || rows < 0 || K < 0)
     return fail(BMM_EINVAL, "pack_operand_kmajor: negative extent");
   // one workgroup per 64 x 64 tile: K / 64 and batch index grid dimensions
-  if (batch > 65535 || rows > kMaxExtent || K >= (int64_t(1) << 22))
-    return fail(BMM_EINVAL, "pack_operand_kmajor: extent too large (batch <= 65535, K < 2^22)");
+  if (batch > 65535 || rows >= (int64_t(1) << 36) || K >= (int64_t(1) << 22))
+    return fail(BMM_EINVAL,
+                "pack_operand_kmajor: extent too large (batch <= 65535, rows < 2^36, K < 2^22)");
   if (rows % atom_rows)
     return fail(BMM_EINVAL,
                 "pack_operand_kmajor: rows (%lld) is not a multiple of atom_rows (%lld)", rows,

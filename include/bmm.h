@@ -116,7 +116,8 @@ int bmm_pack_operand_k8(uint32_t* dst, const uint16_t* src, int64_t batch, int64
  * dst       (batch, rows/R, K/16, R, 8) uint32, contiguous, 16-byte aligned.
  * src       (batch, K, ld_src) 16-bit values, batch stride K*ld_src, 16-byte aligned.
  * rows      multiple of atom_rows; K multiple of 16 and below 2^22; ld_src >= rows and
- *           a multiple of 8; batch at most 65535. Zero batch, rows or K is a no-op.
+ *           a multiple of 8; batch at most 65535; rows below 2^36. Zero batch, rows or K is a
+ *           no-op.
  * Errors: as bmm_pack_operand.
  */
 int bmm_pack_operand_kmajor(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
