@@ -21,10 +21,8 @@
 //
 // Macro tile 256 (M) x 256 (N), 8 waves (two per SIMD) in a 2 x 4 grid, each
 // wave owning a 128 x 64 block of D = 4 x 2 blocks of 32 x 32 (8 accumulators
-// of 16 floats per lane, 128 registers). The two waves of a SIMD run the same
-// pipeline, so while one waits on a load or a barrier the other issues MFMAs.
-// K advances in slabs of 32 values (four 8-value chunks: 2 atoms of k = 16 or
-// 4 of k = 8).
+// of 16 floats per lane, 128 registers). K advances in slabs of 32 values
+// (four 8-value chunks: 2 atoms of k = 16 or 4 of k = 8).
 //
 // Staging takes the role the pages give to TMA box loads ("cp.async.bulk.
 // tensor" page). The LDS image of a slab is fragment-major: 16 A fragments
@@ -39,12 +37,26 @@
 // branches; slabs past the end load as zeros and are multiplied harmlessly.
 // A second grid axis, when present, splits K (split-K form, below).
 //
-// Per slab each wave: the MFMAs of the first 16-value half on fragments already
-// in registers; wait for its own loads of the next slab and its fragment
-// reads; barrier; issue the loads of slab s+4; read the next slab's fragments;
-// the MFMAs of the second half. The barrier is a bare s_barrier after a counted
-// wait, so the loads of later slabs stay in flight across it. C is read and D
-// written with non-temporal accesses (each is touched once).
+// Schedule of the 256 x 256 tile ("ping-pong"): waves 0-3 (group 0, the upper
+// 128 rows) and waves 4-7 (group 1, the lower 128 rows) share the four SIMDs,
+// one wave of each per SIMD. Every slab has two phases, each ended by a
+// workgroup barrier. In phase 0 group 0 issues the 16 MFMAs of the slab
+// back to back while group 1 reads its fragments of the slab from LDS and
+// issues its loads of slab t+3; in phase 1 the roles swap (group 1 multiplies,
+// group 0 reads its fragments of slab t+1 and issues its loads of slab t+4).
+// So on every SIMD one wave keeps the MFMA pipe busy while the other does the
+// memory work and waits, and at a barrier the waiting wave starts its MFMAs
+// while the last ones of the other wave drain. Both groups run the same
+// number of barriers. Each barrier is a bare s_barrier after a counted wait,
+// so loads of later slabs stay in flight across it.
+//
+// The 128 x 128 tile (two workgroups per CU, one wave per SIMD each) keeps a
+// one-group schedule: per slab, the MFMAs of the first 16-value half on
+// fragments already in registers; wait for its own loads of the next slab and
+// its fragment reads; barrier; issue the loads of slab s+4; read the next
+// slab's fragments; the MFMAs of the second half.
+//
+// C is read and D written with non-temporal accesses (each is touched once).
 //
 // Work order: workgroups are dispatched round-robin over the 8 XCDs; the
 // linear tile index is remapped so each XCD receives a contiguous run of
@@ -232,102 +244,211 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
       (((tc.b * p.M_rep + lane_row_atom) * p.N_rep + lane_col_atom) * 16 + (lane & 15)) * 8 +
       4 * (lane >> 5);
   const int64_t d_mstride = p.N_rep * kAtomFloats;  // next M atom
-  if constexpr (kScaled) {
-    // alpha/beta form: the product starts from zero, C is read in the epilogue
+  auto init_acc = [&]() {
+    if constexpr (kScaled) {
+      // alpha/beta form: the product starts from zero, C is read in the epilogue
 #pragma unroll
-    for (int pm = 0; pm < kWaveBlocksM; ++pm)
+      for (int pm = 0; pm < kWaveBlocksM; ++pm)
 #pragma unroll
-      for (int qn = 0; qn < kWaveBlocksN; ++qn) acc[pm][qn] = f32x16{};
-  } else if constexpr (kHasC) {
-    // Blocks outside a ragged last tile read a clamped (valid) address: their
-    // accumulators are never stored, and one branch-free path keeps the 256
-    // accumulator registers in place.
+        for (int qn = 0; qn < kWaveBlocksN; ++qn) acc[pm][qn] = f32x16{};
+    } else if constexpr (kHasC) {
+      auto set4 = [&](int pm, int qn, int q, f32x4 v) {
+        acc[pm][qn][4 * q + 0] = v[0];
+        acc[pm][qn][4 * q + 1] = v[1];
+        acc[pm][qn][4 * q + 2] = v[2];
+        acc[pm][qn][4 * q + 3] = v[3];
+      };
+      if (interior) {
+        // one lane address; the pieces differ by constants and a uniform stride
+        const float* cl = p.C + d_lane;
 #pragma unroll
-    for (int pm = 0; pm < kWaveBlocksM; ++pm)
+        for (int pm = 0; pm < kWaveBlocksM; ++pm)
 #pragma unroll
-      for (int qn = 0; qn < kWaveBlocksN; ++qn)
+          for (int qn = 0; qn < kWaveBlocksN; ++qn)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t ra = lane_row_atom + 2 * pm, ca = lane_col_atom + 4 * qn + q;
-          const int64_t ma = ra < p.M_rep ? ra : p.M_rep - 1;
-          const int64_t na = ca < p.N_rep ? ca : p.N_rep - 1;
-          const f32x4 v = load16f_nt(p.C + (((tc.b * p.M_rep + ma) * p.N_rep + na) * 16 +
-                                            (lane & 15)) * 8 + 4 * (lane >> 5));
-          acc[pm][qn][4 * q + 0] = v[0];
-          acc[pm][qn][4 * q + 1] = v[1];
-          acc[pm][qn][4 * q + 2] = v[2];
-          acc[pm][qn][4 * q + 3] = v[3];
-        }
-  } else {
+            for (int q = 0; q < 4; ++q)
+              set4(pm, qn, q, load16f_nt(cl + 2 * pm * d_mstride + (4 * qn + q) * kAtomFloats));
+      } else {
+        // Blocks outside a ragged last tile read a clamped (valid) address:
+        // their accumulators are never stored.
 #pragma unroll
-    for (int pm = 0; pm < kWaveBlocksM; ++pm)
+        for (int pm = 0; pm < kWaveBlocksM; ++pm)
 #pragma unroll
-      for (int qn = 0; qn < kWaveBlocksN; ++qn)
+          for (int qn = 0; qn < kWaveBlocksN; ++qn)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) acc[pm][qn][e] = p.c_scalar;
-  }
-
-  // Slabs 0..3 into the ring; C (issued first) and slab 0 must have landed.
-  issue(st0, 0);
-  issue(st1, 1);
-  issue(st2, 2);
-  issue(st3, 3);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoadsPerSlab, 15));
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-
-  // Fragments of one slab: [K half][block]. Reads are volatile LDS loads so
-  // they stay where they are written (a half slab ahead of their MFMAs)
-  // instead of being sunk to their first use.
-  using FragB = u32x4[2][kWaveBlocksN];
-  using FragA = u32x4[2][kWaveBlocksM];
-  FragB fb[2];
-  FragA fa[2];
-  auto read_frags = [&](const Stage& st, FragB& b, FragA& a) {
+            for (int q = 0; q < 4; ++q) {
+              const int64_t ra = lane_row_atom + 2 * pm, ca = lane_col_atom + 4 * qn + q;
+              const int64_t ma = ra < p.M_rep ? ra : p.M_rep - 1;
+              const int64_t na = ca < p.N_rep ? ca : p.N_rep - 1;
+              set4(pm, qn, q, load16f_nt(p.C + (((tc.b * p.M_rep + ma) * p.N_rep + na) * 16 +
+                                                (lane & 15)) * 8 + 4 * (lane >> 5)));
+            }
+      }
+    } else {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+      for (int pm = 0; pm < kWaveBlocksM; ++pm)
 #pragma unroll
-      for (int i = 0; i < kWaveBlocksN; ++i)
-        b[j][i] = *(const volatile lds_u32x4*)&st.b[2 * (kWaveBlocksN * wn + i) + j][lane];
+        for (int qn = 0; qn < kWaveBlocksN; ++qn)
 #pragma unroll
-      for (int i = 0; i < kWaveBlocksM; ++i)
-        a[j][i] = *(const volatile lds_u32x4*)&st.a[2 * (kWaveBlocksM * wm + i) + j][lane];
+          for (int e = 0; e < 16; ++e) acc[pm][qn][e] = p.c_scalar;
     }
   };
-  auto mfma_katom = [&](const u32x4 (&b)[kWaveBlocksN], const u32x4 (&a)[kWaveBlocksM]) {
-#pragma unroll
-    for (int pm = 0; pm < kWaveBlocksM; ++pm)
-#pragma unroll
-      for (int qn = 0; qn < kWaveBlocksN; ++qn)
-        acc[pm][qn] = mfma_32x32x16<DT>(b[qn], a[pm], acc[pm][qn]);
-  };
 
-  read_frags(st0, fb[0], fa[0]);
-
-  auto slab = [&](int64_t s, Stage& cur, const Stage& nxt, FragB& bc, FragA& ac, FragB& bn,
-                  FragA& an) {
+  auto sync = [&]() {
     __builtin_amdgcn_sched_barrier(0);
-    mfma_katom(bc[0], ac[0]);
-    // own loads of slab s+1 landed (slabs s+2, s+3 may still be in flight);
-    // own fragment reads of this stage done
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsPerSlab, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("" ::: "memory");
-    issue(cur, s + kStages);
-    read_frags(nxt, bn, an);
-    mfma_katom(bc[1], ac[1]);
-    // The compiler interleaves these: the MFMAs of the second K half go
-    // first, so the pipe has work right after the barrier, with the loads of
-    // slab s+4 and the next slab's fragment reads spread among them.
   };
   const int64_t n_slabs = (kcn + 3) / 4;
-  for (int64_t s = 0; s < n_slabs; s += kStages) {
-    slab(s + 0, st0, st1, fb[0], fa[0], fb[1], fa[1]);
-    slab(s + 1, st1, st2, fb[1], fa[1], fb[0], fa[0]);
-    slab(s + 2, st2, st3, fb[0], fa[0], fb[1], fa[1]);
-    slab(s + 3, st3, st0, fb[1], fa[1], fb[0], fa[0]);
+
+  if constexpr (TM == 256) {
+    // ---- two groups in ping-pong (schedule above) ----
+    // All fragments of one slab for this wave: [K half][B blocks, then A blocks].
+    u32x4 F[2][kWaveBlocksN + kWaveBlocksM];
+    auto read_slab = [&](const Stage& st) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int i = 0; i < kWaveBlocksN; ++i)
+          F[j][i] = *(const volatile lds_u32x4*)&st.b[2 * (kWaveBlocksN * wn + i) + j][lane];
+#pragma unroll
+        for (int i = 0; i < kWaveBlocksM; ++i)
+          F[j][kWaveBlocksN + i] =
+              *(const volatile lds_u32x4*)&st.a[2 * (kWaveBlocksM * wm + i) + j][lane];
+      }
+    };
+    auto mfma_slab = [&]() {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int pm = 0; pm < kWaveBlocksM; ++pm)
+#pragma unroll
+          for (int qn = 0; qn < kWaveBlocksN; ++qn)
+            acc[pm][qn] = mfma_32x32x16<DT>(F[j][qn], F[j][kWaveBlocksN + pm], acc[pm][qn]);
+    };
+    // Ring invariant: a group's own loads of a slab are waited for (counted
+    // vmcnt) in its memory phase two slabs before the slab is read, and the
+    // barrier ending that phase publishes them. A stage is reloaded only in a
+    // phase after both groups' reads of it have completed (lgkmcnt(0)) and a
+    // barrier has passed.
+    // Each group does its own set-up so the register allocator sees two simple
+    // straight-line loops. The group test must be uniform (a scalar branch):
+    // a wave may never run the other group's barriers with its lanes masked off.
+    const bool group0 = __builtin_amdgcn_readfirstlane(wave) < 4;
+    if (group0) {
+      init_acc();
+      issue(st0, 0);
+      issue(st1, 1);
+      issue(st2, 2);
+      issue(st3, 3);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoadsPerSlab, 15));  // C, slab 0 landed
+      sync();
+      read_slab(st0);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsPerSlab, 0));  // slab 1 landed
+      sync();
+      auto slab = [&](int64_t t, Stage& cur, const Stage& next) {
+        mfma_slab();                                                     // phase 0
+        sync();
+        read_slab(next);                                                 // phase 1
+        issue(cur, t + 4);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsPerSlab, 0));  // slab t+2 landed
+        sync();
+      };
+      for (int64_t s = 0; s < n_slabs; s += kStages) {
+        slab(s + 0, st0, st1);
+        slab(s + 1, st1, st2);
+        slab(s + 2, st2, st3);
+        slab(s + 3, st3, st0);
+      }
+    } else {
+      init_acc();
+      issue(st0, 0);
+      issue(st1, 1);
+      issue(st2, 2);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsPerSlab, 15));  // C, slab 0 landed
+      sync();
+      sync();
+      auto slab = [&](int64_t t, Stage& prev, const Stage& cur) {
+        read_slab(cur);                                                  // phase 0
+        issue(prev, t + 3);
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsPerSlab, 0));  // slab t+1 landed
+        sync();
+        mfma_slab();                                                     // phase 1
+        sync();
+      };
+      for (int64_t s = 0; s < n_slabs; s += kStages) {
+        slab(s + 0, st3, st0);
+        slab(s + 1, st0, st1);
+        slab(s + 2, st1, st2);
+        slab(s + 3, st2, st3);
+      }
+    }
+  } else {
+    // ---- one group (128 x 128 tile) ----
+    init_acc();
+    // Slabs 0..3 into the ring; C (issued first) and slab 0 must have landed.
+    issue(st0, 0);
+    issue(st1, 1);
+    issue(st2, 2);
+    issue(st3, 3);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoadsPerSlab, 15));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+
+    // Fragments of one slab: [K half][block]. Reads are volatile LDS loads so
+    // they stay where they are written (a half slab ahead of their MFMAs)
+    // instead of being sunk to their first use.
+    using FragB = u32x4[2][kWaveBlocksN];
+    using FragA = u32x4[2][kWaveBlocksM];
+    FragB fb[2];
+    FragA fa[2];
+    auto read_frags = [&](const Stage& st, FragB& b, FragA& a) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int i = 0; i < kWaveBlocksN; ++i)
+          b[j][i] = *(const volatile lds_u32x4*)&st.b[2 * (kWaveBlocksN * wn + i) + j][lane];
+#pragma unroll
+        for (int i = 0; i < kWaveBlocksM; ++i)
+          a[j][i] = *(const volatile lds_u32x4*)&st.a[2 * (kWaveBlocksM * wm + i) + j][lane];
+      }
+    };
+    auto mfma_katom = [&](const u32x4 (&b)[kWaveBlocksN], const u32x4 (&a)[kWaveBlocksM]) {
+#pragma unroll
+      for (int pm = 0; pm < kWaveBlocksM; ++pm)
+#pragma unroll
+        for (int qn = 0; qn < kWaveBlocksN; ++qn)
+          acc[pm][qn] = mfma_32x32x16<DT>(b[qn], a[pm], acc[pm][qn]);
+    };
+
+    read_frags(st0, fb[0], fa[0]);
+
+    auto slab = [&](int64_t s, Stage& cur, const Stage& nxt, FragB& bc, FragA& ac, FragB& bn,
+                    FragA& an) {
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_katom(bc[0], ac[0]);
+      // own loads of slab s+1 landed (slabs s+2, s+3 may still be in flight);
+      // own fragment reads of this stage done
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsPerSlab, 0));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+      issue(cur, s + kStages);
+      read_frags(nxt, bn, an);
+      mfma_katom(bc[1], ac[1]);
+      // The compiler interleaves these: the MFMAs of the second K half go
+      // first, so the pipe has work right after the barrier, with the loads of
+      // slab s+4 and the next slab's fragment reads spread among them.
+    };
+    const int64_t n_slabs = (kcn + 3) / 4;
+    for (int64_t s = 0; s < n_slabs; s += kStages) {
+      slab(s + 0, st0, st1, fb[0], fa[0], fb[1], fa[1]);
+      slab(s + 1, st1, st2, fb[1], fa[1], fb[0], fa[0]);
+      slab(s + 2, st2, st3, fb[0], fa[0], fb[1], fa[1]);
+      slab(s + 3, st3, st0, fb[1], fa[1], fb[0], fa[0]);
+    }
   }
   // No load may still be writing LDS when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
