@@ -41,14 +41,13 @@ bool direct_fits(int64_t batch, int64_t M_rep, int64_t N_rep) {
 // Shape rule of BMM_KERNEL_AUTO (K counted in values), from a sweep of the
 // kernels over shapes from 16 x 1024 x 1024 to 8192^3 on MI355X:
 // - 256 x 256 LDS tiles when there are at least 128 full ones (3072^3, 144
-//   tiles: 66 us against 69 us with 128 x 128 tiles; 2560^3, 100 tiles, is
-//   faster with the smaller tile);
+//   tiles: 61 us against 69 us with 128 x 128 tiles; 2560^3, 100 tiles, is
+//   faster with the smaller tile, 39 against 49 us);
 // - 128 x 128 LDS tiles when there are at least 128 full ones (2048^3: 24 us
-//   against 42 us with the large tile; 1536^3: 17 against 31 us for the next
-//   best);
+//   against 40 us with the large tile; 1536^3: 17 against 30 us);
 // - otherwise the K-splitting, B-streaming kernel, fastest or tied for every
-//   shape with fewer tiles (1024 x 1024 x 8192: 39 against 58 us;
-//   256 x 4096 x 4096: 24 against 32 us);
+//   shape with fewer tiles (1024 x 1024 x 8192: 41 against 58 us;
+//   256 x 4096 x 4096: 24 against 33 us);
 // - the direct kernel where the others' launch grids would overflow.
 int choose_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K) {
   const int64_t tiles256 = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
@@ -236,11 +235,12 @@ int bmm_mma_tile_opts(float* D, const uint32_t* A, const uint32_t* B, const floa
 
 namespace {
 
-// Macro tile of the split-K form: 128 x 128 up to 16384 K values, 256 x 256
-// beyond. Measured best-over-splits (us, 256 / 128 tiles): 1024 x 1024 x 8192
-// 39.8 / 32.1, 64 x 8192 x 8192 37.0 / 29.4, 2048 x 2048 x 16384 134 / 135,
-// 1024 x 1024 x 65536 144 / 172, 512 x 512 x 65536 65 / 69.
-int splitk_tile(int64_t K) { return K <= 16384 ? 128 : 256; }
+// Macro tile of the split-K form: 128 x 128 below 16384 K values, 256 x 256
+// from there. Measured best-over-splits (us, 256 / 128 tiles): 1024 x 1024 x
+// 8192 37.1 / 32.3, 64 x 8192 x 8192 35.6 / 29.0, 2048 x 2048 x 8192
+// 81.1 / 74.1, 2048 x 2048 x 16384 128.3 / 134.1, 1024 x 1024 x 65536
+// 143.4 / 172.9, 512 x 512 x 65536 62.2 / 69.3.
+int splitk_tile(int64_t K) { return K < 16384 ? 128 : 256; }
 
 }  // namespace
 

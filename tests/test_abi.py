@@ -321,6 +321,10 @@ def test_splitk_workspace_and_default(L):
     assert L.bmm_splitk_default(1, 64, 128, 4096, 16) == 16
     assert L.bmm_splitk_default(1, 512, 1024, 512, 16) == 1
     assert L.bmm_splitk_default(1, 1, 1, 10, 16) == 1
+    # 2048 x 2048: 128 x 128 tiles below K = 16384 (256 tiles, no split), 256 x 256
+    # tiles from K = 16384 (64 tiles, 4 splits)
+    assert L.bmm_splitk_default(1, 128, 256, 1023, 16) == 1
+    assert L.bmm_splitk_default(1, 128, 256, 1024, 16) == 4
     # empty problems need no workspace and launch nothing
     assert splitk(L, D=0, A=0, B=0, M=0, ws=0, ws_bytes=0) == 0
 

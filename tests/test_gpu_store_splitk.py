@@ -112,6 +112,8 @@ SPLIT_CASES = {
     # quarter-integer data: bit-exact against the oracle's split-K form
     "q_272x264x1040_ct": C(1, 272, 264, 1040, "bf16", "quarter", "quarter", c_tensor=True),
     "q_f16_b2_48x40x4112_scalar": C(2, 48, 40, 4112, "f16", "quarter", "quarter", c_scalar=1.25),
+    # K = 16384, where the split-K form switches to 256 x 256 tiles; ragged M and N
+    "q_272x264x16384_ct": C(1, 272, 264, 16384, "bf16", "quarter", "quarter", c_tensor=True),
     # normal data: within bound
     "n_528x264x8208_ct": C(1, 528, 264, 8208, "bf16", c_tensor=True),
 }
