@@ -40,9 +40,11 @@ bool direct_fits(int64_t batch, int64_t M_rep, int64_t N_rep) {
 
 // Shape rule of BMM_KERNEL_AUTO (K counted in values), from a sweep of the
 // kernels over shapes from 16 x 1024 x 1024 to 8192^3 on MI355X:
-// - 256 x 256 LDS tiles when there are at least 128 full ones (3072^3, 144
-//   tiles: 61 us against 69 us with 128 x 128 tiles; 2560^3, 100 tiles, is
-//   faster with the smaller tile, 39 against 49 us);
+// - 256 x 256 LDS tiles when there are more than 128 (3072^3, 144 tiles: 61
+//   us against 69 us with 128 x 128 tiles). With 128 or fewer, the large
+//   tiles leave half the CUs idle while the 512 or fewer small tiles run in one
+//   round at two per CU (8192 x 1024 x 8192, 128 tiles: 144 against 161 us;
+//   2560^3, 100 tiles: 39 against 49 us);
 // - 128 x 128 LDS tiles when there are at least 128 full ones (2048^3: 24 us
 //   against 40 us with the large tile; 1536^3: 17 against 30 us);
 // - otherwise the K-splitting, B-streaming kernel, fastest or tied for every
@@ -52,7 +54,7 @@ bool direct_fits(int64_t batch, int64_t M_rep, int64_t N_rep) {
 int choose_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K) {
   const int64_t tiles256 = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
   const int64_t tiles128 = batch * ((M_rep + 7) / 8) * ((N_rep + 15) / 16);
-  if (M_rep >= 16 && N_rep >= 32 && tiles256 >= 128 && tiled_fits(batch, M_rep, N_rep, K))
+  if (M_rep >= 16 && N_rep >= 32 && tiles256 > 128 && tiled_fits(batch, M_rep, N_rep, K))
     return BMM_KERNEL_TILED;
   if (M_rep >= 8 && N_rep >= 16 && tiles128 >= 128 && tiled_fits(batch, M_rep, N_rep, K, 128))
     return BMM_KERNEL_TILED_128;
@@ -235,12 +237,18 @@ int bmm_mma_tile_opts(float* D, const uint32_t* A, const uint32_t* B, const floa
 
 namespace {
 
-// Macro tile of the split-K form: 128 x 128 below 16384 K values, 256 x 256
-// from there. Measured best-over-splits (us, 256 / 128 tiles): 1024 x 1024 x
-// 8192 37.1 / 32.3, 64 x 8192 x 8192 35.6 / 29.0, 2048 x 2048 x 8192
-// 81.1 / 74.1, 2048 x 2048 x 16384 128.3 / 134.1, 1024 x 1024 x 65536
-// 143.4 / 172.9, 512 x 512 x 65536 62.2 / 69.3.
-int splitk_tile(int64_t K) { return K < 16384 ? 128 : 256; }
+// Macro tile of the split-K form: 256 x 256 from 16384 K values, or when
+// there are at least 128 such tiles (then the default count makes tiles x
+// splits fill the chip one workgroup per CU); 128 x 128 otherwise. Measured
+// best-over-splits (us, 256 / 128 tiles): 1024 x 1024 x 8192 37.1 / 32.3,
+// 64 x 8192 x 8192 35.6 / 29.0, 2048 x 2048 x 8192 81.1 / 74.1, 8192 x 1024
+// x 8192 129.6 (2 splits) / 143.6, 3072 x 3072 x 8192 154.9 / 172.6,
+// 2048 x 2048 x 16384 128.3 / 134.1, 1024 x 1024 x 65536 143.4 / 172.9,
+// 512 x 512 x 65536 62.2 / 69.3.
+int splitk_tile(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K) {
+  const int64_t tiles256 = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
+  return K >= 16384 || tiles256 >= 128 ? 256 : 128;
+}
 
 }  // namespace
 
@@ -269,7 +277,8 @@ int bmm_splitk_default(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_re
   // best or within 10% of best at 1024 x 1024 x 8192, 64 x 8192 x 8192,
   // 2048 x 2048 x 8192, 1024 x 1024 x 65536 and 512 x 512 x 65536).
   const int64_t steps = (K_rep * atom_k + 31) / 32;
-  const int64_t ta = splitk_tile(K_rep * atom_k) / 16, tb = splitk_tile(K_rep * atom_k) / 8;
+  const int tile = splitk_tile(batch, M_rep, N_rep, K_rep * atom_k);
+  const int64_t ta = tile / 16, tb = tile / 8;
   const int64_t tiles = batch * ((M_rep + ta - 1) / ta) * ((N_rep + tb - 1) / tb);
   // (rounded down: 144 tiles stay whole, as two splits would leave a second
   // partial wave of workgroups)
@@ -290,7 +299,7 @@ int bmm_mma_tile_splitk(float* D, const uint32_t* A, const uint32_t* B, const fl
                                      splits, workspace, workspace_bytes);
   if (!st.ok()) return report(st);
   if (batch == 0 || M_rep == 0 || N_rep == 0) return report(st);
-  const int tile = splitk_tile(K_rep * atom_k);
+  const int tile = splitk_tile(batch, M_rep, N_rep, K_rep * atom_k);
   if (!tiled_fits(batch, M_rep, N_rep, K_rep * atom_k, tile)) {
     g_last_error = "mma_tile_splitk: too many macro tiles for one launch";
     return BMM_EINVAL;

@@ -43,11 +43,11 @@ enum {
   BMM_EHIP = -5      /* the HIP runtime reported an error at launch */
 };
 
-/* Kernel selection for bmm_mma_tile_with. AUTO picks by shape (TILED with at
- * least 128 full 256 x 256 tiles, else TILED_128 with at least 128 full
- * 128 x 128 tiles, else SKINNY, else DIRECT if a grid limit rules the others
- * out); the others force one kernel (every kernel accepts every valid shape
- * within its launch-grid limits). */
+/* Kernel selection for bmm_mma_tile_with. AUTO picks by shape (TILED with
+ * more than 128 256 x 256 tiles, ragged ones counted, else TILED_128 with at
+ * least 128 128 x 128 tiles, else SKINNY, else DIRECT if a grid limit rules
+ * the others out); the others force one kernel (every kernel accepts every
+ * valid shape within its launch-grid limits). */
 typedef enum {
   BMM_KERNEL_AUTO = 0,
   BMM_KERNEL_DIRECT = 1, /* one wave per 16x16 output block, operands straight from HBM */
@@ -337,8 +337,8 @@ int64_t bmm_mma_splitk_workspace_bytes(int64_t batch, int64_t M_rep, int64_t N_r
 
 /* A split count for bmm_mma_tile_splitk: enough tiles x splits for every CU,
  * each split at least 1024 K values deep, at most 32; 1 when splitting does
- * not pay. (The split-K form uses 128 x 128 tiles below K = 16384 values and
- * 256 x 256 tiles from there.) */
+ * not pay. (The split-K form uses 256 x 256 tiles from K = 16384 values or
+ * when there are at least 128 of them, and 128 x 128 tiles otherwise.) */
 int bmm_splitk_default(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep,
                        int32_t atom_k);
 

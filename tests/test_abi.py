@@ -163,6 +163,11 @@ def test_plain_entry_point_validates(L):
 
 def test_select_kernel(L):
     assert L.bmm_select_kernel(-1, 1, 1, 1) == EINVAL
+    # 256 x 256 tiles only above 128 of them: 8192 x 1024 (128 tiles) takes
+    # 128 x 128 tiles, 3072^3 (144 tiles) and 8192^3 the large ones
+    assert L.bmm_select_kernel(1, 512, 128, 512) == 4
+    assert L.bmm_select_kernel(1, 192, 384, 192) == 2
+    assert L.bmm_select_kernel(1, 512, 1024, 512) == 2
     for shape in [(1, 1, 1, 2), (1, 8, 16, 16), (1, 256, 512, 256), (1, 1, 2048, 1024),
                   (1, 512, 1024, 512)]:
         assert L.bmm_select_kernel(*shape) in (1, 2, 3, 4)
@@ -325,6 +330,8 @@ def test_splitk_workspace_and_default(L):
     # tiles from K = 16384 (64 tiles, 4 splits)
     assert L.bmm_splitk_default(1, 128, 256, 1023, 16) == 1
     assert L.bmm_splitk_default(1, 128, 256, 1024, 16) == 4
+    # 8192 x 1024 x 8192: 128 tiles of 256 x 256 below K = 16384 too, 2 splits
+    assert L.bmm_splitk_default(1, 512, 128, 512, 16) == 2
     # empty problems need no workspace and launch nothing
     assert splitk(L, D=0, A=0, B=0, M=0, ws=0, ws_bytes=0) == 0
 

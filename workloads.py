@@ -113,6 +113,12 @@ EXTRA_WORKLOADS = {
     for w in [
         Workload("deep_k_1024x1024x65536_bf16_ctensor", 1, 1024, 1024, 65536, BF16, "normal",
                  "normal", c_tensor=True),
+        # one GPU's share of the 8192^3 multiply split 8 ways along N (all of A, an
+        # eighth of the columns of B, C and D), and along M
+        Workload("shard_n8_8192x1024x8192_bf16_ctensor", 1, 8192, 1024, 8192, BF16, "normal",
+                 "normal", c_tensor=True),
+        Workload("shard_m8_1024x8192x8192_bf16_ctensor", 1, 1024, 8192, 8192, BF16, "normal",
+                 "normal", c_tensor=True),
     ]
 }
 
