@@ -125,8 +125,6 @@ def main():
     ap.add_argument("--splitk", type=int, default=None,
                     help="run the split-K form with this many splits (0: the library's default)")
     args = ap.parse_args()
-    if args.kmajor and args.atom_k != 16:
-        ap.error("--kmajor packs the k = 16 layout only")
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

@@ -92,6 +92,7 @@ def lib():
         L.bmm_pack_operand.argtypes = [p, p, i64, i64, i64, i64, i32, p]
         L.bmm_pack_operand_kmajor.argtypes = [p, p, i64, i64, i64, i64, i32, p]
         L.bmm_pack_operand_k8.argtypes = [p, p, i64, i64, i64, i64, i32, p]
+        L.bmm_pack_operand_kmajor_k8.argtypes = [p, p, i64, i64, i64, i64, i32, p]
         L.bmm_mma_tile_opts.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64, i64,
                                         ctypes.c_int, ctypes.POINTER(MmaOpts), p]
         L.bmm_box_copy.argtypes = [p, p, ctypes.POINTER(BoxDesc), ctypes.POINTER(i64), p]
@@ -111,6 +112,7 @@ def lib():
         L.bmm_mma_splitk_workspace_bytes.restype = i64
         L.bmm_splitk_default.argtypes = [i64, i64, i64, i64, i32]
         for f in (L.bmm_pack_operand, L.bmm_pack_operand_kmajor, L.bmm_pack_operand_k8,
+                  L.bmm_pack_operand_kmajor_k8,
                   L.bmm_box_copy, L.bmm_mma_tile, L.bmm_mma_tile_with, L.bmm_mma_tile_scaled,
                   L.bmm_mma_tile_opts, L.bmm_select_kernel, L.bmm_box_store,
                   L.bmm_box_reduce_add, L.bmm_mma_tile_splitk, L.bmm_splitk_default):
@@ -172,10 +174,13 @@ def pack_operand(x: torch.Tensor, atom_rows: int, K: int | None = None,
 
 
 def pack_operand_kmajor(xt: torch.Tensor, atom_rows: int, rows: int | None = None,
-                        out: torch.Tensor | None = None) -> torch.Tensor:
+                        out: torch.Tensor | None = None, atom_k: int = 16) -> torch.Tensor:
     """K-major (batch, K, ld) or (K, ld) 16-bit tensor holding element (row, k)
-    at [b, k, row] -> packed words (batch, rows/R, K/16, R, 8) int32, the same
-    words pack_operand gives for the row-major matrix. rows defaults to ld."""
+    at [b, k, row] -> packed words (batch, rows/R, K/atom_k, R, atom_k/2) int32,
+    the same words pack_operand gives for the row-major matrix (atom_k 16, or 8
+    for bmm_pack_operand_kmajor_k8). rows defaults to ld."""
+    if atom_k not in (16, 8):
+        raise ValueError("pack_operand_kmajor: atom_k must be 16 or 8")
     _require_cuda(xt)
     if xt.element_size() != 2:
         raise ValueError("pack_operand_kmajor takes 16-bit (f16/bf16 bit) tensors")
@@ -186,13 +191,13 @@ def pack_operand_kmajor(xt: torch.Tensor, atom_rows: int, rows: int | None = Non
             (batch > 1 and xt.stride(0) != K * ld):
         raise ValueError("pack_operand_kmajor: source must be (batch, K, ld) with dense strides")
     rows = ld if rows is None else rows
-    shape = (batch, rows // atom_rows, K // 16, atom_rows, 8)
+    shape = (batch, rows // atom_rows, K // atom_k, atom_rows, atom_k // 2)
     if out is None:
         out = torch.empty(shape, dtype=torch.int32, device=xt.device)
     elif tuple(out.shape) != shape or not out.is_contiguous() or out.element_size() != 4:
         raise ValueError(f"pack_operand_kmajor: out must be a contiguous 32-bit tensor of shape {shape}")
-    _check(lib().bmm_pack_operand_kmajor(_ptr(out), _ptr(xt), batch, rows, K, ld, atom_rows,
-                                         _stream(xt)))
+    fn = lib().bmm_pack_operand_kmajor if atom_k == 16 else lib().bmm_pack_operand_kmajor_k8
+    _check(fn(_ptr(out), _ptr(xt), batch, rows, K, ld, atom_rows, _stream(xt)))
     return out
 
 

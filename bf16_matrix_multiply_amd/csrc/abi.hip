@@ -116,12 +116,22 @@ int bmm_pack_operand_k8(uint32_t* dst, const uint16_t* src, int64_t batch, int64
 
 int bmm_pack_operand_kmajor(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
                             int64_t K, int64_t ld_src, int32_t atom_rows, void* stream) {
-  bmm::Status st = bmm::check_pack_kmajor(dst, src, batch, rows, K, ld_src, atom_rows);
+  bmm::Status st = bmm::check_pack_kmajor(dst, src, batch, rows, K, ld_src, atom_rows, 16);
   if (!st.ok()) return report(st);
   if (batch == 0 || rows == 0 || K == 0) return report(st);
-  return hip_status(bmm::launch_pack_kmajor(dst, src, batch, rows, K, ld_src, atom_rows,
+  return hip_status(bmm::launch_pack_kmajor(dst, src, batch, rows, K, ld_src, atom_rows, 16,
                                             static_cast<hipStream_t>(stream)),
                     "pack_operand_kmajor launch");
+}
+
+int bmm_pack_operand_kmajor_k8(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
+                               int64_t K, int64_t ld_src, int32_t atom_rows, void* stream) {
+  bmm::Status st = bmm::check_pack_kmajor(dst, src, batch, rows, K, ld_src, atom_rows, 8);
+  if (!st.ok()) return report(st);
+  if (batch == 0 || rows == 0 || K == 0) return report(st);
+  return hip_status(bmm::launch_pack_kmajor(dst, src, batch, rows, K, ld_src, atom_rows, 8,
+                                            static_cast<hipStream_t>(stream)),
+                    "pack_operand_kmajor_k8 launch");
 }
 
 int bmm_box_copy(void* dst_image, const void* src, const bmm_box_desc* desc,

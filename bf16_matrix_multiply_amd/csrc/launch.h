@@ -45,7 +45,7 @@ __device__ inline int b_lane_words(int atom_k, int row, int g) {
 hipError_t launch_pack(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
                        int64_t K, int64_t ld, int R, int atom_k, hipStream_t s);
 hipError_t launch_pack_kmajor(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
-                              int64_t K, int64_t ld, int R, hipStream_t s);
+                              int64_t K, int64_t ld, int R, int atom_k, hipStream_t s);
 hipError_t launch_box(void* dst, const void* src, const bmm_box_desc& d, hipStream_t s);
 // Store (elem_type 0) or add reduction of a compact image into a global box.
 hipError_t launch_box_store(void* dst, const void* img, const bmm_box_desc& d, int elem_type,

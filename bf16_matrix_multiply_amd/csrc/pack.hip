@@ -92,11 +92,12 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(uint32_t* __restrict
 // lanes read 16-byte pieces of source rows (8 consecutive rows at one k,
 // coalesced), a barrier, then each lane gathers the 8 consecutive K values of
 // one row from the tile and stores them as one 16-byte packed chunk, the
-// chunks of the tile in destination order (contiguous stores).
+// chunks of the tile in destination order (contiguous stores). The chunk is
+// half a row of a 16-deep atom, or a whole row of an 8-deep one (KA = 8).
 constexpr int kTile = 64;
 constexpr int kTilePitch = kTile + 8;  // u16 per LDS row (16-byte aligned rows)
 
-template <int R>
+template <int R, int KA>
 __global__ __launch_bounds__(256) void pack_kmajor_kernel(uint32_t* __restrict__ dst,
                                                           const uint16_t* __restrict__ src,
                                                           int64_t rows, int64_t K, int64_t ld) {
@@ -116,20 +117,24 @@ __global__ __launch_bounds__(256) void pack_kmajor_kernel(uint32_t* __restrict__
   }
   __syncthreads();
   constexpr int kLog2R = R == 16 ? 4 : 3;
-  const int64_t rows_rep = rows / R, K_rep = K / 16;
+  const int64_t rows_rep = rows / R, K_rep = K / KA;
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int c = tid + 256 * u;
-    // chunk c of the tile: row block c / (8R), then K atom, row in atom, half
+    // chunk c of the tile: row block c / (8R), then K atom, row in atom, and
+    // (KA = 16) half of the atom row
     const int rb = c >> (kLog2R + 3), rem = c & (8 * R - 1);
-    const int kr = rem >> (kLog2R + 1), i = (rem >> 1) & (R - 1), h = rem & 1;
-    const int row_l = rb * R + i, k_l = kr * 16 + h * 8;
+    const int kr = KA == 16 ? rem >> (kLog2R + 1) : rem >> kLog2R;
+    const int i = KA == 16 ? (rem >> 1) & (R - 1) : rem & (R - 1);
+    const int h = KA == 16 ? rem & 1 : 0;
+    const int row_l = rb * R + i, k_l = kr * KA + h * 8;
     if (row0 + row_l >= rows || k0 + k_l >= K) continue;
     u32x4 w;
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       w[e] = uint32_t(tile[k_l + 2 * e][row_l]) | (uint32_t(tile[k_l + 2 * e + 1][row_l]) << 16);
-    const int64_t off = (((b * rows_rep + row0 / R + rb) * K_rep + k0 / 16 + kr) * R + i) * 8 + 4 * h;
+    const int64_t off = (((b * rows_rep + row0 / R + rb) * K_rep + k0 / KA + kr) * R + i) *
+                            (KA / 2) + 4 * h;
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(dst + off));
   }
 }
@@ -137,13 +142,12 @@ __global__ __launch_bounds__(256) void pack_kmajor_kernel(uint32_t* __restrict__
 }  // namespace
 
 hipError_t launch_pack_kmajor(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
-                              int64_t K, int64_t ld, int R, hipStream_t s) {
+                              int64_t K, int64_t ld, int R, int atom_k, hipStream_t s) {
   const dim3 grid(unsigned((rows + kTile - 1) / kTile), unsigned((K + kTile - 1) / kTile),
                   unsigned(batch));
-  if (R == 16)
-    hipLaunchKernelGGL(pack_kmajor_kernel<16>, grid, dim3(256), 0, s, dst, src, rows, K, ld);
-  else
-    hipLaunchKernelGGL(pack_kmajor_kernel<8>, grid, dim3(256), 0, s, dst, src, rows, K, ld);
+  auto kern = R == 16 ? (atom_k == 16 ? pack_kmajor_kernel<16, 16> : pack_kmajor_kernel<16, 8>)
+                      : (atom_k == 16 ? pack_kmajor_kernel<8, 16> : pack_kmajor_kernel<8, 8>);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, dst, src, rows, K, ld);
   return hipGetLastError();
 }
 

@@ -73,7 +73,7 @@ Status check_pack(const uint32_t* dst, const uint16_t* src, int64_t batch, int64
 }
 
 Status check_pack_kmajor(const uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
-                         int64_t K, int64_t ld_src, int32_t atom_rows) {
+                         int64_t K, int64_t ld_src, int32_t atom_rows, int32_t atom_k) {
   if (atom_rows != 16 && atom_rows != 8)
     return fail(BMM_EINVAL, "pack_operand_kmajor: atom_rows must be 16 (A) or 8 (B), got %lld",
                 atom_rows);
@@ -87,7 +87,8 @@ Status check_pack_kmajor(const uint32_t* dst, const uint16_t* src, int64_t batch
     return fail(BMM_EINVAL,
                 "pack_operand_kmajor: rows (%lld) is not a multiple of atom_rows (%lld)", rows,
                 atom_rows);
-  if (K % 16) return fail(BMM_EINVAL, "pack_operand_kmajor: K (%lld) is not a multiple of 16", K);
+  if (K % atom_k)
+    return fail(BMM_EINVAL, "pack_operand_kmajor: K (%lld) is not a multiple of %lld", K, atom_k);
   if (ld_src < rows)
     return fail(BMM_EINVAL, "pack_operand_kmajor: ld_src (%lld) < rows (%lld)", ld_src, rows);
   if (ld_src > (int64_t(1) << 32)) return fail(BMM_EINVAL, "pack_operand_kmajor: ld_src too large");

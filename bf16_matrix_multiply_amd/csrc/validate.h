@@ -19,7 +19,8 @@ Status check_pack(const uint32_t* dst, const uint16_t* src, int64_t batch, int64
                   int64_t K, int64_t ld_src, int32_t atom_rows, int32_t atom_k);
 
 Status check_pack_kmajor(const uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
-                         int64_t K, int64_t ld_src, int32_t atom_rows);
+                         int64_t K, int64_t ld_src, int32_t atom_rows,
+                         int32_t atom_k);
 
 Status check_box(const void* dst, const void* src, const bmm_box_desc* d);
 

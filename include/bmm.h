@@ -124,6 +124,25 @@ int bmm_pack_operand_kmajor(uint32_t* dst, const uint16_t* src, int64_t batch, i
                             int64_t K, int64_t ld_src, int32_t atom_rows, void* stream);
 
 /*
+ * bmm_pack_operand_kmajor_k8 — K-major source to the m16n8k8 layout.
+ *
+ * The two preparations above together: a K-major (transposed) source, as for
+ * bmm_pack_operand_kmajor, packed into atoms with an atom K of 8, as for
+ * bmm_pack_operand_k8 (mma.sync page: "Accumulation, transpose and
+ * alpha/beta"; the m16n8k8 form of the introduction and the table of shapes).
+ * The result is exactly what bmm_pack_operand_k8 gives for the row-major
+ * matrix:
+ *
+ *   dst[b, r, kr, i, w] = src[b, 8*kr+2*w, R*r+i] | src[b, 8*kr+2*w+1, R*r+i] << 16
+ *
+ * dst  (batch, rows/R, K/8, R, 4) uint32, contiguous, 16-byte aligned.
+ * K    a multiple of 8 and below 2^22. Every other argument, and the errors, as
+ *      bmm_pack_operand_kmajor.
+ */
+int bmm_pack_operand_kmajor_k8(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
+                               int64_t K, int64_t ld_src, int32_t atom_rows, void* stream);
+
+/*
  * bmm_box_copy — a rectangular global box through an LDS image.
  *
  * The role of the TMA tile-mode box load on the cp.async.bulk.tensor page

@@ -200,6 +200,31 @@ def test_pack_kmajor_empty_is_noop(L):
     assert pack_km(L, dst=0, src=0, K=0) == 0
 
 
+def pack_km8(L, dst=P0, src=P1, batch=1, rows=16, K=24, ld=16, R=16):
+    return L.bmm_pack_operand_kmajor_k8(dst, src, batch, rows, K, ld, R, None)
+
+
+@pytest.mark.parametrize("kw,code,needle", [
+    (dict(R=4), EINVAL, "atom_rows"),
+    (dict(rows=24, ld=24, R=16), EINVAL, "multiple of atom_rows"),
+    (dict(K=20), EINVAL, "multiple of 8"),
+    (dict(ld=8), EINVAL, "ld_src"),
+    (dict(ld=20), EALIGN, "multiple of 8"),
+    (dict(K=1 << 22), EINVAL, "too large"),
+    (dict(dst=P0 + 4), EALIGN, "aligned"),
+    (dict(dst=P1 + 32), EOVERLAP, "overlaps"),
+])
+def test_pack_kmajor_k8_rejects(L, kw, code, needle):
+    assert pack_km8(L, **kw) == code
+    assert needle in err(L)
+
+
+def test_pack_kmajor_k8_takes_k_multiple_of_8(L):
+    # K = 24 is a whole number of 8-deep atoms, which the k = 16 form rejects
+    assert pack_km8(L, dst=0, src=0, batch=0, K=24) == 0
+    assert pack_km(L, K=24) == EINVAL
+
+
 def pack_k8(L, dst=P0, src=P1, batch=1, rows=16, K=24, ld=24, R=16):
     return L.bmm_pack_operand_k8(dst, src, batch, rows, K, ld, R, None)
 

@@ -73,6 +73,29 @@ def test_pack_kmajor_shapes(R, rows, K, ld):
     assert np.array_equal(got, oracle.pack_kmajor(xt, R, rows))
 
 
+@pytest.mark.parametrize("R", [16, 8])
+def test_pack_kmajor_k8_all_bit_patterns(R):
+    """K-major source into the m16n8k8 layout: every bit pattern lands where
+    the oracle's k = 8 packer puts it for the row-major matrix."""
+    xt = np.arange(1 << 17, dtype=np.uint32).astype(np.uint16).reshape(2, 256, 256)
+    got = gu.host_u32(bmm.pack_operand_kmajor(gu.dev_u16(xt), R, atom_k=8))
+    assert np.array_equal(got, oracle.pack_k8(np.swapaxes(xt, 1, 2), R))
+
+
+@pytest.mark.parametrize("R,rows,K,ld", [(16, 16, 8, 16), (8, 8, 24, 40), (16, 48, 72, 96),
+                                         (8, 200, 328, 208), (16, 272, 1032, 272),
+                                         (16, 64, 64, 64), (8, 72, 136, 80)])
+def test_pack_kmajor_k8_shapes(R, rows, K, ld):
+    """k = 8 from K-major sources: ragged 64x64 tiles, K an odd number of
+    8-deep atoms, ld > rows, batch 3; equal to the row-major k = 8 packer's
+    words on the logical matrix."""
+    rng = np.random.default_rng(rows * 11 + K)
+    xt = util.random_bits(rng, (3, K, ld))
+    got = gu.host_u32(bmm.pack_operand_kmajor(gu.dev_u16(xt), R, rows=rows, atom_k=8))
+    x = np.ascontiguousarray(np.swapaxes(xt, 1, 2)[:, :rows, :])
+    assert np.array_equal(got, oracle.pack_k8(x, R))
+
+
 def test_pack_kmajor_equals_rowmajor_pack_full_size():
     """At 8192x8192 (A) and 16384x16384 (B): packing the K-major copy gives
     the same words as packing the row-major matrix, and the oracle's words."""
@@ -84,6 +107,8 @@ def test_pack_kmajor_equals_rowmajor_pack_full_size():
         got = bmm.pack_operand_kmajor(xtd, R)
         ref = bmm.pack_operand(xd, R)
         assert torch.equal(got, ref), (rows, K)
+        assert torch.equal(bmm.pack_operand_kmajor(xtd, R, atom_k=8),
+                           bmm.pack_operand(xd, R, atom_k=8)), (rows, K, 8)
         if rows == 8192:
             assert np.array_equal(gu.host_u32(got), oracle.pack(x, R))
         del x, xd, xtd, got, ref
