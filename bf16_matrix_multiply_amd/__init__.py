@@ -159,8 +159,9 @@ def pack_operand(x: torch.Tensor, atom_rows: int, K: int | None = None,
     if x.dim() == 2:
         x = x.unsqueeze(0)
     batch, rows, ld = x.shape
-    if x.stride(2) != 1 or (rows > 1 and x.stride(1) != ld) or \
-            (batch > 1 and x.stride(0) != rows * ld):
+    # (an empty source has nothing to pack; torch gives it arbitrary strides)
+    if x.numel() and (x.stride(2) != 1 or (rows > 1 and x.stride(1) != ld) or
+                      (batch > 1 and x.stride(0) != rows * ld)):
         raise ValueError("pack_operand: source must be (batch, rows, ld) with dense strides")
     K = ld if K is None else K
     shape = (batch, rows // atom_rows, K // atom_k, atom_rows, atom_k // 2)
@@ -187,8 +188,8 @@ def pack_operand_kmajor(xt: torch.Tensor, atom_rows: int, rows: int | None = Non
     if xt.dim() == 2:
         xt = xt.unsqueeze(0)
     batch, K, ld = xt.shape
-    if xt.stride(2) != 1 or (K > 1 and xt.stride(1) != ld) or \
-            (batch > 1 and xt.stride(0) != K * ld):
+    if xt.numel() and (xt.stride(2) != 1 or (K > 1 and xt.stride(1) != ld) or
+                       (batch > 1 and xt.stride(0) != K * ld)):
         raise ValueError("pack_operand_kmajor: source must be (batch, K, ld) with dense strides")
     rows = ld if rows is None else rows
     shape = (batch, rows // atom_rows, K // atom_k, atom_rows, atom_k // 2)
