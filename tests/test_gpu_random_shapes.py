@@ -62,3 +62,22 @@ def test_random_shape_all_forms(w):
         D = bmm.mma_tile_splitk(A, B, C, c, w.dtype, 3, out=out).cpu().numpy()
         bad = np.argwhere(D.view(np.uint32) != ref.view(np.uint32))
         assert bad.size == 0, f"{w.name} k={ka} split-K: {len(bad)} mismatches, first {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("w", CASES[:8], ids=[w.name for w in CASES[:8]])
+def test_random_shape_scaled(w):
+    """alpha/beta form with alpha = 0.5, beta = -1.5: on quarter-integer data
+    every term is exact and fma(alpha, P, fl(beta * C)) rounds nothing, so each
+    kernel must give the oracle's bits."""
+    inp = workloads.make_inputs(w, seed=9)
+    Ao, Bo = gu.oracle_operands(w, inp)
+    ref = oracle.mma_scaled(Ao, Bo, inp["c_tensor"], inp["c_scalar"], 0.5, -1.5, w.dtype)
+    A = bmm.pack_operand(gu.dev_u16(inp["a"]), 16)
+    B = bmm.pack_operand(gu.dev_u16(inp["b"]), 8)
+    C = None if inp["c_tensor"] is None else torch.from_numpy(inp["c_tensor"]).cuda()
+    for kernel in KERNELS:
+        out = torch.full((w.batch, w.M_rep, w.N_rep, 16, 8), float("nan"), device="cuda")
+        D = bmm.mma_tile(A, B, C, float(inp["c_scalar"]), w.dtype, out=out, kernel=kernel,
+                         alpha=0.5, beta=-1.5).cpu().numpy()
+        bad = np.argwhere(D.view(np.uint32) != ref.view(np.uint32))
+        assert bad.size == 0, f"{w.name} {kernel} scaled: {len(bad)} mismatches, first {bad[:3].tolist()}"
