@@ -7,16 +7,20 @@
 // this little-endian machine), so packing is a permutation of 16-byte chunks:
 // output chunk (row block rb, c) with c = (kr, i, h) comes from source row
 // R*rb + i, K offset 16*kr + 8*h (with an atom K of 8: c = (kr, i), K offset
-// 8*kr). A block takes 1024 consecutive output chunks; the order in which its
-// lanes take them (below) keeps both the row reads and the chunk writes in
-// runs of 128 bytes or more.
+// 8*kr).
 //
-// Stores: a packed operand of up to 128 MiB (half the 256 MB Infinity Cache)
-// is written through the caches, so the multiply that reads it next finds
-// part of it there (8192^3 bf16: packs 4% and the whole step 1-4% faster than
-// with streaming stores); a larger one is written with non-temporal stores,
-// which do not flush the caches the multiply then streams through (16 x 16384
-// x 16384: the skinny multiply 87 us against 115 us after cached stores).
+// Two kernels, chosen by the size of the packed operand:
+// - up to 128 MiB (half the 256 MB Infinity Cache), pack_staged_kernel: lanes
+//   read whole 1 KB runs of one source row, the chunks are permuted through
+//   LDS, and the workgroup's 32 KB output span is written contiguously through
+//   the caches, so the multiply that reads it next finds part of it there
+//   (8192^3 bf16: the whole step 3% faster than with pack_kernel and
+//   streaming stores);
+// - above that, pack_kernel (no LDS; row pieces of 128 bytes, 256-byte output
+//   runs) with non-temporal stores, which do not flush the caches the
+//   multiply then streams through (16 x 16384 x 16384: the skinny multiply
+//   87 us, against 115 us after cached stores; this kernel also packs a
+//   512 MiB operand 1-4% faster than the staged one).
 #include "common.h"
 #include "launch.h"
 
@@ -24,12 +28,15 @@ namespace bmm {
 namespace {
 
 constexpr int kPackThreads = 256;
-constexpr int64_t kCachedPackBytes = int64_t(128) << 20;  // packed bytes stored through the caches
+constexpr int64_t kCachedPackBytes = int64_t(128) << 20;  // largest output of the staged kernel
 constexpr int kPackUnroll = 4;
 // The 16-row chunk order below is a permutation of 4 waves x 4 iterations x 64 lanes.
 static_assert(kPackThreads == 256 && kPackUnroll == 4, "chunk order assumes 1024 chunks per block");
 
-template <int R, int KA, bool kCachedStore>
+// pack_kernel: a block takes 1024 consecutive output chunks; the order in
+// which its lanes take them (below) keeps both the row reads and the chunk
+// writes in runs of 128 bytes or more.
+template <int R, int KA>
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(uint32_t* __restrict__ dst,
                                                             const uint16_t* __restrict__ src,
                                                             int64_t rb0, int32_t chunks_per_rb,
@@ -77,12 +84,61 @@ __global__ __launch_bounds__(kPackThreads) void pack_kernel(uint32_t* __restrict
 #pragma unroll
   for (int u = 0; u < kPackUnroll; ++u) {
     const int32_t c = cs[u];
-    if (c < chunks_per_rb) {
-      if constexpr (kCachedStore)
-        *reinterpret_cast<u32x4*>(drb + int64_t(c) * 4) = v[u];
-      else
-        __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(drb + int64_t(c) * 4));
+    if (c < chunks_per_rb)
+      __builtin_nontemporal_store(v[u], reinterpret_cast<u32x4*>(drb + int64_t(c) * 4));
+  }
+}
+
+// ---- operands up to 128 MiB: staged through LDS ----
+constexpr int kStagedThreads = 512;
+constexpr int kStagedUnroll = 4;
+constexpr int kSpan = kStagedThreads * kStagedUnroll;  // output chunks (16 B) per workgroup
+constexpr int kLog2Span = 11;
+static_assert(kSpan == 1 << kLog2Span, "span is a power of two");
+
+template <int R, int KA>
+__global__ __launch_bounds__(kStagedThreads) void pack_staged_kernel(
+    uint32_t* __restrict__ dst, const uint16_t* __restrict__ src, int64_t rb0,
+    int32_t chunks_per_rb, int64_t ld) {
+  // One workgroup: row block rb and the kSpan output chunks (32 KB) of one K
+  // span of 8 * kSpan / R values. Its source is R row pieces of 32 KB / R
+  // each, so consecutive lanes read consecutive 16 bytes of one row; every
+  // chunk goes to its output position in LDS, and the span is written out
+  // contiguously.
+  constexpr int kLog2R = R == 16 ? 4 : 3;
+  constexpr int kRowChunks = kSpan / R;               // source chunks per row of the span
+  constexpr int kLog2RowChunks = kLog2Span - kLog2R;
+  constexpr int kShift = KA == 16 ? kLog2R + 1 : kLog2R;  // log2(chunks per K atom)
+  constexpr int kMask = kShift >= 4 ? 15 : (1 << kShift) - 1;
+  __shared__ __attribute__((aligned(16))) u32x4 lds[kSpan];
+  // LDS slot of output chunk o: its low bits XORed with the K atom above them,
+  // so that the strided writes below spread over the banks (a bijection: only
+  // bits below kShift change, as a function of the bits from kShift up).
+  auto slot = [](int o) { return o ^ ((o >> kShift) & kMask); };
+
+  const int64_t rb = rb0 + blockIdx.y;
+  const int32_t span0 = blockIdx.x * kSpan;           // first output chunk of the span
+  const int32_t n_out = chunks_per_rb - span0 < kSpan ? chunks_per_rb - span0 : kSpan;
+  const int64_t k0 = int64_t(blockIdx.x) * (8 * kRowChunks);  // first K value of the span
+  const int64_t K = int64_t(chunks_per_rb) * 8 / R;
+  const uint16_t* srow = src + rb * R * ld + k0;
+#pragma unroll
+  for (int u = 0; u < kStagedUnroll; ++u) {
+    const int q = u * kStagedThreads + threadIdx.x;   // source chunk: row i, piece kc
+    const int i = q >> kLog2RowChunks, kc = q & (kRowChunks - 1);
+    if (k0 + 8 * kc < K) {
+      const u32x4 v = load16_nt(reinterpret_cast<const uint32_t*>(srow + i * ld + 8 * kc));
+      // output chunk: K atom, row in atom, half (k = 16) or K atom, row (k = 8)
+      const int o = KA == 16 ? (((kc >> 1) << kLog2R) + i) * 2 + (kc & 1) : (kc << kLog2R) + i;
+      lds[slot(o)] = v;
     }
+  }
+  __syncthreads();
+  uint32_t* dspan = dst + (rb * int64_t(chunks_per_rb) + span0) * 4;
+#pragma unroll
+  for (int u = 0; u < kStagedUnroll; ++u) {
+    const int o = u * kStagedThreads + threadIdx.x;
+    if (o < n_out) *reinterpret_cast<u32x4*>(dspan + int64_t(o) * 4) = lds[slot(o)];
   }
 }
 
@@ -155,16 +211,17 @@ hipError_t launch_pack(uint32_t* dst, const uint16_t* src, int64_t batch, int64_
                        int64_t K, int64_t ld, int R, int atom_k, hipStream_t s) {
   const int64_t n_rb = batch * (rows / R);
   const int32_t chunks = int32_t(R * (K / 8));  // 16-byte chunks per row block
-  const int per_block = kPackThreads * kPackUnroll;
+  const bool staged = batch * rows * K * 2 <= kCachedPackBytes;
+  const int per_block = staged ? kSpan : kPackThreads * kPackUnroll;
   const unsigned gx = unsigned((chunks + per_block - 1) / per_block);
+  auto kern = staged ? (R == 16 ? (atom_k == 16 ? pack_staged_kernel<16, 16> : pack_staged_kernel<16, 8>)
+                                : (atom_k == 16 ? pack_staged_kernel<8, 16> : pack_staged_kernel<8, 8>))
+                     : (R == 16 ? (atom_k == 16 ? pack_kernel<16, 16> : pack_kernel<16, 8>)
+                                : (atom_k == 16 ? pack_kernel<8, 16> : pack_kernel<8, 8>));
+  const unsigned threads = staged ? kStagedThreads : kPackThreads;
   for (int64_t rb0 = 0; rb0 < n_rb; rb0 += 65535) {
     const unsigned gy = unsigned(n_rb - rb0 < 65535 ? n_rb - rb0 : 65535);
-    const bool cached = batch * rows * K * 2 <= kCachedPackBytes;
-    auto kern = cached ? (R == 16 ? (atom_k == 16 ? pack_kernel<16, 16, true> : pack_kernel<16, 8, true>)
-                                  : (atom_k == 16 ? pack_kernel<8, 16, true> : pack_kernel<8, 8, true>))
-                       : (R == 16 ? (atom_k == 16 ? pack_kernel<16, 16, false> : pack_kernel<16, 8, false>)
-                                  : (atom_k == 16 ? pack_kernel<8, 16, false> : pack_kernel<8, 8, false>));
-    hipLaunchKernelGGL(kern, dim3(gx, gy), dim3(kPackThreads), 0, s, dst, src, rb0, chunks, ld);
+    hipLaunchKernelGGL(kern, dim3(gx, gy), dim3(threads), 0, s, dst, src, rb0, chunks, ld);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -33,7 +33,8 @@ KERNEL_SOURCES = {
     "mma_tile": ["mma_direct.hip", "mma_tiled.hip", "mma_skinny.hip", "common.h", "launch.h"],
     "pack_operand": ["pack.hip", "common.h"],
 }
-KERNEL_MATCH = {"mma_tile": "mma_", "pack_operand": "pack_kernel"}
+# Dispatch-name prefixes of each kernel family (inside the bmm namespace).
+KERNEL_MATCH = {"mma_tile": ("mma_",), "pack_operand": ("pack_kernel<", "pack_staged_kernel<")}
 
 
 def _code_only(text: str) -> str:
@@ -121,7 +122,7 @@ def summarize(fetch_csv, write_csv, workload, kernel):
         copy_ids = [i for i, (n, _) in d.items() if "copy" in n.lower()]
         copy_kib = d[copy_ids[0]][1]
         scale = (COPY_BYTES / 1024) / copy_kib if copy_kib > 0 else float("nan")
-        mine = [v for i, (n, v) in d.items() if KERNEL_MATCH[kernel] in n]
+        mine = [v for i, (n, v) in d.items() if any(m in n for m in KERNEL_MATCH[kernel])]
         # one launch of the multiply per step; packing is two launches per
         # step (A and B), counted together as bench.py's pack roofline does
         per_step = 1 if kernel == "mma_tile" else 2
