@@ -27,7 +27,32 @@ struct BoxParams {
   int64_t dims[5], strides[5], coords[5], step[5];
   int32_t box[5];
   int32_t box_elems;
+  // 16-byte path (see box_chunk_path): chunks in the box, chunks per
+  // innermost box row, elements per chunk
+  int32_t box_chunks, inner_chunks, vlen, vec;
 };
+
+constexpr int kChunkUnroll = 4;  // 16-byte chunks a lane has in flight
+
+// Global byte offset of 16-byte chunk c of repeat t, and whether it lies
+// inside the tensor (with the 16-byte path a chunk is wholly inside or
+// wholly outside: see box_chunk_path).
+__device__ __forceinline__ int64_t chunk_offset(const BoxParams& p, int64_t t, int32_t c,
+                                                bool& inside) {
+  const int in = p.rank - 1;
+  int32_t row = c / p.inner_chunks;
+  const int64_t gi = p.coords[in] + t * p.step[in] + int64_t(c - row * p.inner_chunks) * p.vlen;
+  inside = gi >= 0 && gi < p.dims[in];
+  int64_t off = gi * p.eb;
+  for (int d = in - 1; d >= 0; --d) {
+    const int32_t j = row % p.box[d];
+    row /= p.box[d];
+    const int64_t g = p.coords[d] + t * p.step[d] + j;
+    inside = inside && g >= 0 && g < p.dims[d];
+    off += g * p.strides[d];
+  }
+  return off;
+}
 
 template <typename T>
 __device__ __forceinline__ void copy_in(const char* src, char* lds, const BoxParams& p,
@@ -54,6 +79,39 @@ __device__ __forceinline__ void copy_out(char* dst, const char* lds, const BoxPa
   T* out = reinterpret_cast<T*>(dst) + t * p.box_elems;
   for (int32_t e = threadIdx.x; e < p.box_elems; e += kBoxThreads)
     out[e] = *reinterpret_cast<const T*>(lds + swizzle_offset(uint32_t(e) * sizeof(T), p.swizzle));
+}
+
+// Box load, 16 bytes per lane: chunks read from global memory (zero outside
+// the tensor), written to the swizzled LDS image, read back and stored compact.
+__global__ __launch_bounds__(kBoxThreads) void box_kernel_v(char* __restrict__ dst,
+                                                            const char* __restrict__ src,
+                                                            BoxParams p) {
+  extern __shared__ __attribute__((aligned(128))) char lds[];
+  const int64_t t = blockIdx.x;
+  const int32_t n = p.box_chunks;
+  for (int32_t c0 = threadIdx.x; c0 < n; c0 += kBoxThreads * kChunkUnroll) {
+    u32x4 v[kChunkUnroll];
+#pragma unroll
+    for (int u = 0; u < kChunkUnroll; ++u) {
+      const int32_t c = c0 + u * kBoxThreads;
+      v[u] = u32x4{0u, 0u, 0u, 0u};
+      if (c < n) {
+        bool inside;
+        const int64_t off = chunk_offset(p, t, c, inside);
+        if (inside) v[u] = load16(reinterpret_cast<const uint32_t*>(src + off));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kChunkUnroll; ++u) {
+      const int32_t c = c0 + u * kBoxThreads;
+      if (c < n)
+        *reinterpret_cast<u32x4*>(lds + swizzle_offset(uint32_t(c) * 16, p.swizzle)) = v[u];
+    }
+  }
+  __syncthreads();
+  u32x4* out = reinterpret_cast<u32x4*>(dst + t * int64_t(n) * 16);
+  for (int32_t c = threadIdx.x; c < n; c += kBoxThreads)
+    out[c] = *reinterpret_cast<const u32x4*>(lds + swizzle_offset(uint32_t(c) * 16, p.swizzle));
 }
 
 __global__ __launch_bounds__(kBoxThreads) void box_kernel(char* __restrict__ dst,
@@ -151,6 +209,97 @@ __global__ __launch_bounds__(kBoxThreads) void box_store_kernel(char* __restrict
   }
 }
 
+// Lane-wise add of a 16-byte chunk with the element semantics of add_elem.
+template <int ET>
+__device__ __forceinline__ u32x4 add_chunk(u32x4 g, u32x4 v) {
+  // Whole-vector operations or scalar copies only: a bit cast applied to an element of an
+  // ext_vector_type operand does not reliably read that element.
+  u32x4 r = g;
+  if constexpr (ET == BMM_ELEM_F32) {
+    r = __builtin_bit_cast(u32x4, __builtin_bit_cast(f32x4, g) + __builtin_bit_cast(f32x4, v));
+  } else if constexpr (ET == BMM_ELEM_I32) {
+    r = g + v;
+  } else if constexpr (ET == BMM_ELEM_I64) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint64_t a = uint64_t(g[2 * e]) | (uint64_t(g[2 * e + 1]) << 32);
+      const uint64_t b = uint64_t(v[2 * e]) | (uint64_t(v[2 * e + 1]) << 32);
+      const uint64_t s = a + b;
+      r[2 * e] = uint32_t(s);
+      r[2 * e + 1] = uint32_t(s >> 32);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint16_t lo, hi;
+      const uint16_t glo = uint16_t(g[e]), ghi = uint16_t(g[e] >> 16);
+      const uint16_t vlo = uint16_t(v[e]), vhi = uint16_t(v[e] >> 16);
+      if constexpr (ET == BMM_ELEM_F16) {
+        lo = __builtin_bit_cast(uint16_t, _Float16(float(__builtin_bit_cast(_Float16, glo)) +
+                                                   float(__builtin_bit_cast(_Float16, vlo))));
+        hi = __builtin_bit_cast(uint16_t, _Float16(float(__builtin_bit_cast(_Float16, ghi)) +
+                                                   float(__builtin_bit_cast(_Float16, vhi))));
+      } else {
+        lo = bf16_rne(bf16_value(glo) + bf16_value(vlo));
+        hi = bf16_rne(bf16_value(ghi) + bf16_value(vhi));
+      }
+      r[e] = uint32_t(lo) | (uint32_t(hi) << 16);
+    }
+  }
+  return r;
+}
+
+// Box store (ET = 0) or add reduction, 16 bytes per lane.
+template <int ET>
+__global__ __launch_bounds__(kBoxThreads) void box_store_kernel_v(char* __restrict__ dst,
+                                                                  const char* __restrict__ img,
+                                                                  BoxParams p, int64_t t0) {
+  extern __shared__ __attribute__((aligned(128))) char lds[];
+  const int64_t t = t0 + blockIdx.x;
+  const int32_t n = p.box_chunks;
+  const u32x4* in = reinterpret_cast<const u32x4*>(img + t * int64_t(n) * 16);
+  for (int32_t c = threadIdx.x; c < n; c += kBoxThreads)
+    *reinterpret_cast<u32x4*>(lds + swizzle_offset(uint32_t(c) * 16, p.swizzle)) = in[c];
+  __syncthreads();
+  for (int32_t c0 = threadIdx.x; c0 < n; c0 += kBoxThreads * kChunkUnroll) {
+    int64_t off[kChunkUnroll];
+    bool ok[kChunkUnroll];
+    u32x4 g[kChunkUnroll];
+#pragma unroll
+    for (int u = 0; u < kChunkUnroll; ++u) {
+      const int32_t c = c0 + u * kBoxThreads;
+      ok[u] = false;
+      off[u] = 0;
+      if (c < n) off[u] = chunk_offset(p, t, c, ok[u]);
+      if constexpr (ET != 0) {
+        if (ok[u]) g[u] = load16(reinterpret_cast<const uint32_t*>(dst + off[u]));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kChunkUnroll; ++u) {
+      if (!ok[u]) continue;
+      const int32_t c = c0 + u * kBoxThreads;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + swizzle_offset(uint32_t(c) * 16, p.swizzle));
+      if constexpr (ET == 0)
+        *reinterpret_cast<u32x4*>(dst + off[u]) = v;
+      else
+        *reinterpret_cast<u32x4*>(dst + off[u]) = add_chunk<ET>(g[u], v);
+    }
+  }
+}
+
+// The 16-byte path applies when every 16-byte chunk of every repeat is
+// aligned in global memory and wholly inside or wholly outside the tensor:
+// the innermost box row, start coordinate, coordinate step and tensor extent
+// are all whole chunks (outer strides and base are 16-byte aligned by
+// validation).
+bool box_chunk_path(const bmm_box_desc& d) {
+  const int in = d.rank - 1;
+  const int64_t eb = d.elem_bytes;
+  return (d.box[in] * eb) % 16 == 0 && (d.coords[in] * eb) % 16 == 0 &&
+         (d.coord_step[in] * eb) % 16 == 0 && (d.dims[in] * eb) % 16 == 0;
+}
+
 BoxParams box_params(const bmm_box_desc& d) {
   BoxParams p{};
   p.rank = d.rank;
@@ -166,6 +315,10 @@ BoxParams box_params(const bmm_box_desc& d) {
     elems *= d.box[i];
   }
   p.box_elems = int32_t(elems);
+  p.vec = box_chunk_path(d) ? 1 : 0;
+  p.vlen = 16 / d.elem_bytes;
+  p.box_chunks = int32_t(elems * d.elem_bytes / 16);
+  p.inner_chunks = int32_t(int64_t(d.box[d.rank - 1]) * d.elem_bytes / 16);
   return p;
 }
 
@@ -176,7 +329,16 @@ hipError_t launch_box_store(void* dst, const void* img, const bmm_box_desc& d, i
   const BoxParams p = box_params(d);
   const size_t lds_bytes = size_t((int64_t(p.box_elems) * d.elem_bytes + 127) / 128 * 128);
   void (*kern)(char*, const char*, BoxParams, int64_t) = nullptr;
-  switch (elem_type) {
+  if (p.vec) {
+    switch (elem_type) {
+      case BMM_ELEM_F32: kern = box_store_kernel_v<BMM_ELEM_F32>; break;
+      case BMM_ELEM_F16: kern = box_store_kernel_v<BMM_ELEM_F16>; break;
+      case BMM_ELEM_BF16: kern = box_store_kernel_v<BMM_ELEM_BF16>; break;
+      case BMM_ELEM_I32: kern = box_store_kernel_v<BMM_ELEM_I32>; break;
+      case BMM_ELEM_I64: kern = box_store_kernel_v<BMM_ELEM_I64>; break;
+      default: kern = box_store_kernel_v<0>; break;
+    }
+  } else switch (elem_type) {
     case BMM_ELEM_F32: kern = box_store_kernel<float, BMM_ELEM_F32>; break;
     case BMM_ELEM_F16: kern = box_store_kernel<uint16_t, BMM_ELEM_F16>; break;
     case BMM_ELEM_BF16: kern = box_store_kernel<uint16_t, BMM_ELEM_BF16>; break;
@@ -211,8 +373,9 @@ hipError_t launch_box(void* dst, const void* src, const bmm_box_desc& d, hipStre
   const int64_t elems = p.box_elems;
   // The swizzle keeps every offset inside its 128-byte row: round the image up.
   const size_t lds_bytes = size_t((elems * d.elem_bytes + 127) / 128 * 128);
-  hipLaunchKernelGGL(box_kernel, dim3(unsigned(d.n_repeat)), dim3(kBoxThreads), lds_bytes, s,
-                     static_cast<char*>(dst), static_cast<const char*>(src), p);
+  hipLaunchKernelGGL(p.vec ? box_kernel_v : box_kernel, dim3(unsigned(d.n_repeat)),
+                     dim3(kBoxThreads), lds_bytes, s, static_cast<char*>(dst),
+                     static_cast<const char*>(src), p);
   return hipGetLastError();
 }
 

@@ -155,6 +155,38 @@ def test_box_matches_oracle(case, swizzle):
     assert np.array_equal(img.cpu().numpy().view(x.dtype), ref)
 
 
+# 16-byte-path descriptors (every chunk wholly inside or outside), partly
+# outside the tensor in every dimension, inner dimension included
+CHUNK_BOX_CASES = [
+    (np.uint32, (20, 48), (8, 16), (-4, -8), 4, (6, 12)),
+    (np.uint16, (6, 5, 40), (3, 4, 16), (4, -2, -8), 3, (-2, 3, 24)),
+    (np.uint8, (3, 80), (2, 48), (1, -16), 3, (1, 48)),
+    (np.int64, (9, 12), (3, 4), (-1, -2), 3, (4, 6)),
+    (np.uint32, (2, 130, 64), (1, 64, 64), (0, -32, 0), 5, (1, 64, 0)),
+]
+
+
+def chunk_path(itemsize, shape, box, coords, step):
+    """Whether the library takes its 16-byte box path for this descriptor:
+    innermost box row, start, step and extent all whole 16-byte chunks."""
+    return all((v * itemsize) % 16 == 0 for v in (box[-1], coords[-1], step[-1], shape[-1]))
+
+
+@pytest.mark.parametrize("swizzle", [0, 1, 3])
+@pytest.mark.parametrize("case", range(len(CHUNK_BOX_CASES)))
+def test_box_chunk_path_matches_oracle(case, swizzle):
+    dtype, shape, box, coords, rep, step = CHUNK_BOX_CASES[case]
+    assert chunk_path(np.dtype(dtype).itemsize, shape, box, coords, step)
+    rng = np.random.default_rng(100 + case)
+    x = rng.integers(1, 120, shape).astype(dtype)
+    ref, ref_bytes = oracle.box_copy(x, box, coords, rep, step)
+    xd = torch.from_numpy(x.view({1: np.uint8, 2: np.int16, 4: np.int32, 8: np.int64}[x.itemsize])).cuda()
+    img, nbytes = bmm.box_copy(xd, box, coords, rep, step, swizzle=swizzle)
+    torch.cuda.synchronize()
+    assert nbytes == ref_bytes
+    assert np.array_equal(img.cpu().numpy().view(x.dtype), ref)
+
+
 def test_box_errors_leave_output():
     x = torch.arange(256, dtype=torch.int32, device="cuda").reshape(16, 16)
     out = torch.full((1, 8, 16), -1, dtype=torch.int32, device="cuda")

@@ -66,6 +66,67 @@ def test_box_store(case, swizzle):
     assert nbytes == ref_bytes
 
 
+# 16-byte-path descriptors: partly outside in every dimension; the last two
+# have overlapping repeats (launched one after another)
+CHUNK_STORE_CASES = [
+    (np.uint32, (20, 48), (8, 16), (-4, -8), 4, (6, 12)),
+    (np.uint16, (6, 5, 40), (3, 4, 16), (4, -2, -8), 3, (-2, 3, 24)),
+    (np.uint8, (3, 80), (2, 48), (1, -16), 3, (1, 48)),
+    (np.uint64, (9, 12), (3, 4), (-1, -2), 3, (4, 6)),
+    (np.uint32, (16, 64), (8, 32), (2, 8), 3, (1, 4)),
+    (np.uint16, (12, 64), (4, 32), (-1, 8), 4, (2, -8)),
+]
+
+
+def chunk_path(itemsize, shape, box, coords, step):
+    """Whether the library takes its 16-byte box path for this descriptor."""
+    return all((v * itemsize) % 16 == 0 for v in (box[-1], coords[-1], step[-1], shape[-1]))
+
+
+@pytest.mark.parametrize("swizzle", [0, 2])
+@pytest.mark.parametrize("case", range(len(CHUNK_STORE_CASES)))
+def test_box_store_chunk_path(case, swizzle):
+    dtype, shape, box, coords, rep, step = CHUNK_STORE_CASES[case]
+    assert chunk_path(np.dtype(dtype).itemsize, shape, box, coords, step)
+    rng = np.random.default_rng(50 + case)
+    G = rng.integers(1, 200, shape).astype(dtype)
+    img = rng.integers(1, 200, (rep, *box)).astype(dtype)
+    Gd = _dev(G)
+    nbytes = bmm.box_store(Gd, _dev(img), box, coords, rep, step, swizzle=swizzle)
+    ref, ref_bytes = oracle.box_store(G, img, box, coords, rep, step)
+    assert np.array_equal(_host(Gd, dtype), ref)
+    assert nbytes == ref_bytes
+
+
+@pytest.mark.parametrize("etype", ["f32", "f16", "bf16", "i32", "i64"])
+@pytest.mark.parametrize("overlap", [False, True])
+def test_box_reduce_add_chunk_path(etype, overlap):
+    """The 16-byte add path on random finite operands (ties, subnormals,
+    overflow to inf for 16-bit types; wrap-around for integers), partly outside
+    in both dimensions; with overlap, repeats add into the same elements in
+    order."""
+    rng = np.random.default_rng(77)
+    eb = {"f32": 4, "f16": 2, "bf16": 2, "i32": 4, "i64": 8}[etype]
+    shape, box, coords = (40, 64), (16, 32), (30, -16)
+    rep, step = (3, (1, 16)) if overlap else (2, (16, 48))
+    assert chunk_path(eb, shape, box, coords, step)
+    if etype == "f32":
+        G = (rng.standard_normal(shape) * 1e3).astype(np.float32)
+        img = rng.standard_normal((rep, *box)).astype(np.float32)
+    elif etype in ("f16", "bf16"):
+        G, img = _finite_bits(rng, shape, etype), _finite_bits(rng, (rep, *box), etype)
+    else:
+        it = np.int32 if etype == "i32" else np.int64
+        info = np.iinfo(it)
+        G = rng.integers(info.min, info.max, shape, dtype=it)
+        img = rng.integers(info.min, info.max, (rep, *box), dtype=it)
+    Gd = _dev(G)
+    bmm.box_reduce_add(Gd, _dev(img), box, coords, etype, rep, step, swizzle=1)
+    ref, _ = oracle.box_store(G, img, box, coords, rep, step, op="add", elem_type=etype)
+    got = _host(Gd, G.dtype)
+    assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), etype
+
+
 def _finite_bits(rng, shape, dt):
     bits = rng.integers(0, 1 << 16, shape, dtype=np.uint32).astype(np.uint16)
     ones = 0x7C00 if dt == "f16" else 0x7F80
