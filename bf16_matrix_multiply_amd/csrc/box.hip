@@ -32,7 +32,17 @@ struct BoxParams {
   int32_t box_chunks, inner_chunks, vlen, vec;
 };
 
-constexpr int kChunkUnroll = 4;  // 16-byte chunks a lane has in flight
+constexpr int kChunkUnroll = 4;        // 16-byte chunks a lane has in flight
+constexpr int kChunkThreadsMax = 1024;  // 16-byte path: lanes per workgroup at most
+
+// 16-byte path workgroup size: enough lanes that each has at most
+// kChunkUnroll chunks of its box (one round of loads in flight), in whole
+// wavefronts. A 64 KB box takes 1024 lanes; two such workgroups fill a CU's LDS.
+inline int chunk_threads(int32_t box_chunks) {
+  const int32_t per = (box_chunks + kChunkUnroll - 1) / kChunkUnroll;
+  const int32_t t = (per + 63) / 64 * 64;
+  return t < 64 ? 64 : (t > kChunkThreadsMax ? kChunkThreadsMax : t);
+}
 
 // Global byte offset of 16-byte chunk c of repeat t, and whether it lies
 // inside the tensor (with the 16-byte path a chunk is wholly inside or
@@ -83,35 +93,39 @@ __device__ __forceinline__ void copy_out(char* dst, const char* lds, const BoxPa
 
 // Box load, 16 bytes per lane: chunks read from global memory (zero outside
 // the tensor), written to the swizzled LDS image, read back and stored compact.
-__global__ __launch_bounds__(kBoxThreads) void box_kernel_v(char* __restrict__ dst,
-                                                            const char* __restrict__ src,
-                                                            BoxParams p) {
+// One round per lane, as in box_store_kernel_v.
+__global__ __launch_bounds__(kChunkThreadsMax) void box_kernel_v(char* __restrict__ dst,
+                                                                 const char* __restrict__ src,
+                                                                 BoxParams p) {
   extern __shared__ __attribute__((aligned(128))) char lds[];
   const int64_t t = blockIdx.x;
   const int32_t n = p.box_chunks;
-  for (int32_t c0 = threadIdx.x; c0 < n; c0 += kBoxThreads * kChunkUnroll) {
-    u32x4 v[kChunkUnroll];
+  const int32_t nt = blockDim.x;
+  u32x4 v[kChunkUnroll];
 #pragma unroll
-    for (int u = 0; u < kChunkUnroll; ++u) {
-      const int32_t c = c0 + u * kBoxThreads;
-      v[u] = u32x4{0u, 0u, 0u, 0u};
-      if (c < n) {
-        bool inside;
-        const int64_t off = chunk_offset(p, t, c, inside);
-        if (inside) v[u] = load16(reinterpret_cast<const uint32_t*>(src + off));
-      }
+  for (int u = 0; u < kChunkUnroll; ++u) {
+    const int32_t c = int32_t(threadIdx.x) + u * nt;
+    v[u] = u32x4{0u, 0u, 0u, 0u};
+    if (c < n) {
+      bool inside;
+      const int64_t off = chunk_offset(p, t, c, inside);
+      if (inside) v[u] = load16(reinterpret_cast<const uint32_t*>(src + off));
     }
+  }
 #pragma unroll
-    for (int u = 0; u < kChunkUnroll; ++u) {
-      const int32_t c = c0 + u * kBoxThreads;
-      if (c < n)
-        *reinterpret_cast<u32x4*>(lds + swizzle_offset(uint32_t(c) * 16, p.swizzle)) = v[u];
-    }
+  for (int u = 0; u < kChunkUnroll; ++u) {
+    const int32_t c = int32_t(threadIdx.x) + u * nt;
+    if (c < n)
+      *reinterpret_cast<u32x4*>(lds + swizzle_offset(uint32_t(c) * 16, p.swizzle)) = v[u];
   }
   __syncthreads();
   u32x4* out = reinterpret_cast<u32x4*>(dst + t * int64_t(n) * 16);
-  for (int32_t c = threadIdx.x; c < n; c += kBoxThreads)
-    out[c] = *reinterpret_cast<const u32x4*>(lds + swizzle_offset(uint32_t(c) * 16, p.swizzle));
+#pragma unroll
+  for (int u = 0; u < kChunkUnroll; ++u) {
+    const int32_t c = int32_t(threadIdx.x) + u * nt;
+    if (c < n)
+      out[c] = *reinterpret_cast<const u32x4*>(lds + swizzle_offset(uint32_t(c) * 16, p.swizzle));
+  }
 }
 
 __global__ __launch_bounds__(kBoxThreads) void box_kernel(char* __restrict__ dst,
@@ -249,42 +263,51 @@ __device__ __forceinline__ u32x4 add_chunk(u32x4 g, u32x4 v) {
   return r;
 }
 
-// Box store (ET = 0) or add reduction, 16 bytes per lane.
+// Box store (ET = 0) or add reduction, 16 bytes per lane. A box holds at most
+// kChunkThreadsMax * kChunkUnroll chunks (64 KB), so each lane takes one round:
+// its image chunks and, for the add, the destination chunks they land on are
+// all requested before the barrier, and the adds and stores follow it.
 template <int ET>
-__global__ __launch_bounds__(kBoxThreads) void box_store_kernel_v(char* __restrict__ dst,
-                                                                  const char* __restrict__ img,
-                                                                  BoxParams p, int64_t t0) {
+__global__ __launch_bounds__(kChunkThreadsMax) void box_store_kernel_v(char* __restrict__ dst,
+                                                                       const char* __restrict__ img,
+                                                                       BoxParams p, int64_t t0) {
   extern __shared__ __attribute__((aligned(128))) char lds[];
   const int64_t t = t0 + blockIdx.x;
   const int32_t n = p.box_chunks;
+  const int32_t nt = blockDim.x;
   const u32x4* in = reinterpret_cast<const u32x4*>(img + t * int64_t(n) * 16);
-  for (int32_t c = threadIdx.x; c < n; c += kBoxThreads)
-    *reinterpret_cast<u32x4*>(lds + swizzle_offset(uint32_t(c) * 16, p.swizzle)) = in[c];
-  __syncthreads();
-  for (int32_t c0 = threadIdx.x; c0 < n; c0 += kBoxThreads * kChunkUnroll) {
-    int64_t off[kChunkUnroll];
-    bool ok[kChunkUnroll];
-    u32x4 g[kChunkUnroll];
+  int64_t off[kChunkUnroll];
+  bool ok[kChunkUnroll];
+  u32x4 v[kChunkUnroll], g[kChunkUnroll];
 #pragma unroll
-    for (int u = 0; u < kChunkUnroll; ++u) {
-      const int32_t c = c0 + u * kBoxThreads;
-      ok[u] = false;
-      off[u] = 0;
-      if (c < n) off[u] = chunk_offset(p, t, c, ok[u]);
+  for (int u = 0; u < kChunkUnroll; ++u) {
+    const int32_t c = int32_t(threadIdx.x) + u * nt;
+    ok[u] = false;
+    off[u] = 0;
+    if (c < n) {
+      v[u] = in[c];
+      off[u] = chunk_offset(p, t, c, ok[u]);
       if constexpr (ET != 0) {
         if (ok[u]) g[u] = load16(reinterpret_cast<const uint32_t*>(dst + off[u]));
       }
     }
+  }
 #pragma unroll
-    for (int u = 0; u < kChunkUnroll; ++u) {
-      if (!ok[u]) continue;
-      const int32_t c = c0 + u * kBoxThreads;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + swizzle_offset(uint32_t(c) * 16, p.swizzle));
-      if constexpr (ET == 0)
-        *reinterpret_cast<u32x4*>(dst + off[u]) = v;
-      else
-        *reinterpret_cast<u32x4*>(dst + off[u]) = add_chunk<ET>(g[u], v);
-    }
+  for (int u = 0; u < kChunkUnroll; ++u) {
+    const int32_t c = int32_t(threadIdx.x) + u * nt;
+    if (c < n)
+      *reinterpret_cast<u32x4*>(lds + swizzle_offset(uint32_t(c) * 16, p.swizzle)) = v[u];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < kChunkUnroll; ++u) {
+    if (!ok[u]) continue;
+    const int32_t c = int32_t(threadIdx.x) + u * nt;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(lds + swizzle_offset(uint32_t(c) * 16, p.swizzle));
+    if constexpr (ET == 0)
+      *reinterpret_cast<u32x4*>(dst + off[u]) = x;
+    else
+      *reinterpret_cast<u32x4*>(dst + off[u]) = add_chunk<ET>(g[u], x);
   }
 }
 
@@ -319,6 +342,8 @@ BoxParams box_params(const bmm_box_desc& d) {
   p.vlen = 16 / d.elem_bytes;
   p.box_chunks = int32_t(elems * d.elem_bytes / 16);
   p.inner_chunks = int32_t(int64_t(d.box[d.rank - 1]) * d.elem_bytes / 16);
+  // the 16-byte kernels cover a box in one round of kChunkUnroll chunks per lane
+  if (p.box_chunks > kChunkThreadsMax * kChunkUnroll) p.vec = 0;
   return p;
 }
 
@@ -354,14 +379,15 @@ hipError_t launch_box_store(void* dst, const void* img, const bmm_box_desc& d, i
   }
   char* out = static_cast<char*>(dst);
   const char* in = static_cast<const char*>(img);
+  const unsigned threads = unsigned(p.vec ? chunk_threads(p.box_chunks) : kBoxThreads);
   if (repeats_disjoint) {
-    hipLaunchKernelGGL(kern, dim3(unsigned(d.n_repeat)), dim3(kBoxThreads), lds_bytes, s, out, in,
-                       p, int64_t(0));
+    hipLaunchKernelGGL(kern, dim3(unsigned(d.n_repeat)), dim3(threads), lds_bytes, s, out, in, p,
+                       int64_t(0));
     return hipGetLastError();
   }
   // overlapping repeats: one launch each, in repeat order
   for (int64_t t = 0; t < d.n_repeat; ++t) {
-    hipLaunchKernelGGL(kern, dim3(1), dim3(kBoxThreads), lds_bytes, s, out, in, p, t);
+    hipLaunchKernelGGL(kern, dim3(1), dim3(threads), lds_bytes, s, out, in, p, t);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -373,8 +399,9 @@ hipError_t launch_box(void* dst, const void* src, const bmm_box_desc& d, hipStre
   const int64_t elems = p.box_elems;
   // The swizzle keeps every offset inside its 128-byte row: round the image up.
   const size_t lds_bytes = size_t((elems * d.elem_bytes + 127) / 128 * 128);
+  const unsigned threads = unsigned(p.vec ? chunk_threads(p.box_chunks) : kBoxThreads);
   hipLaunchKernelGGL(p.vec ? box_kernel_v : box_kernel, dim3(unsigned(d.n_repeat)),
-                     dim3(kBoxThreads), lds_bytes, s, static_cast<char*>(dst),
+                     dim3(threads), lds_bytes, s, static_cast<char*>(dst),
                      static_cast<const char*>(src), p);
   return hipGetLastError();
 }

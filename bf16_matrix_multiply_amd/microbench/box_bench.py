@@ -6,7 +6,9 @@ Each operation streams a 512 MiB float32 tensor, seen as (rows, 256), through
 the rows: one workgroup per box, through an LDS image in each swizzle mode.
 Prints one JSON line per operation: time per call (HIP events), the bytes it
 moves (copy and store: read + write of the image; add: image + destination
-read, destination write) and the fraction of the 8 TB/s HBM peak.
+read, destination write) and the fraction of the 8 TB/s HBM peak. Two
+context lines time torch's own elementwise copy and in-place add over the
+same bytes, the practical streaming rate on the same box.
 
     python3 -m bf16_matrix_multiply_amd.microbench.box_bench [--reps 10]
 """
@@ -47,6 +49,15 @@ def main():
     img = torch.empty((n, box_rows, cols), device="cuda")
     image_bytes = n * box_rows * cols * 4
     box, coords, step = (box_rows, cols), (0, 0), (box_rows, 0)
+    flat = g.view(n, box_rows, cols)
+    for name, fn, nbytes in (("torch_copy", lambda: img.copy_(flat), 2 * image_bytes),
+                             ("torch_add_", lambda: flat.add_(img), 3 * image_bytes)):
+        mean, med, mn = timed(fn, args.reps)
+        gbs = nbytes / (mean * 1e-6) / 1e9
+        print(json.dumps({"op": name, "bytes_per_call": nbytes, "us_mean": round(mean, 1),
+                          "us_median": round(med, 1), "us_min": round(mn, 1),
+                          "gbs": round(gbs, 1), "frac_of_8tbs": round(gbs / PEAK_GBS, 4)}),
+              flush=True)
     for swz in (0, 3):
         ops = {
             "box_copy": (lambda: bmm.box_copy(g, box, coords, n, step, swizzle=swz, out=img),
