@@ -224,6 +224,30 @@ def test_mid_size_tiled128_sampled(shape, kernel):
     gu.assert_parity_sampled(wq, inpq, Dq)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_tile_shapes_bitwise(dtype):
+    """Normal data, ragged M and N, an odd K_rep: the 256 x 256 and the
+    128 x 128 tile each give every 32 x 32 block of D the C value first and
+    then one 32x32x16 MFMA per K atom pair in ascending K, so the two agree
+    bit for bit. The split-K form with a single split forms the partial sum
+    from zero and then adds C once, so it gives fl(C + P) with P the product
+    that either tile gives for a scalar C of 0."""
+    w = C(1, 528, 264, 2064, dtype, c_tensor=True, name=f"tiles_{dtype}")
+    inp = workloads.make_inputs(w, seed=6)
+    A, B, Cd, D256 = gu.gpu_run(w, inp, "tiled")
+    _, _, _, D128 = gu.gpu_run(w, inp, "tiled128")
+    assert np.array_equal(D256.view(np.uint32), D128.view(np.uint32))
+    gu.assert_parity_full(w, inp, D256, "tiled")
+    P = {k: bmm.mma_tile(A, B, None, 0.0, dtype, kernel=k).cpu().numpy()
+         for k in ("tiled", "tiled128")}
+    assert np.array_equal(P["tiled"].view(np.uint32), P["tiled128"].view(np.uint32))
+    out = torch.full(D256.shape, float("nan"), device="cuda")
+    D1 = bmm.mma_tile_splitk(A, B, Cd, 0.0, dtype, 1, out=out).cpu().numpy()
+    ref1 = inp["c_tensor"] + P["tiled"]
+    assert ref1.dtype == np.float32
+    assert np.array_equal(D1.view(np.uint32), ref1.view(np.uint32))
+
+
 # ---- alpha/beta form (bmm_mma_tile_scaled) ----
 
 SCALED = {
