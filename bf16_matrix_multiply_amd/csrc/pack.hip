@@ -144,42 +144,56 @@ __global__ __launch_bounds__(kStagedThreads) void pack_staged_kernel(
 
 // ---- K-major sources ----
 // The source holds the transpose: element (row, k) at src[b, k, row], rows
-// contiguous. One workgroup turns a 64-row x 64-K tile around through LDS:
-// lanes read 16-byte pieces of source rows (8 consecutive rows at one k,
-// coalesced), a barrier, then each lane gathers the 8 consecutive K values of
-// one row from the tile and stores them as one 16-byte packed chunk, the
-// chunks of the tile in destination order (contiguous stores). The chunk is
+// contiguous. One workgroup turns a tile of kKmTileRows rows x 64 K values
+// around through LDS: lanes read 16-byte pieces of source rows (consecutive
+// lanes along one k, so each k contributes a run of 2 * kKmTileRows bytes), a
+// barrier, then each lane gathers the 8 consecutive K values of one row from
+// the tile and stores them as one 16-byte packed chunk, the chunks of the tile
+// in destination order (runs of one row block's 64 K values). The chunk is
 // half a row of a 16-deep atom, or a whole row of an 8-deep one (KA = 8).
 // Outputs up to 128 MiB are stored through the caches, as by the staged row-
 // major packer (8192^2 bf16: each K-major pack 17% faster, and the multiply
-// after it 3%); larger ones with non-temporal stores.
-constexpr int kTile = 64;
-constexpr int kTilePitch = kTile + 8;  // u16 per LDS row (16-byte aligned rows)
+// after it 3%); larger ones with non-temporal stores. Measured at 8192^2 in
+// one process: plain source loads 2-5% faster than non-temporal ones; tiles
+// of 128 or 256 rows 4% and 70% slower than 64; taking the K tiles first, or
+// groups of 8 row tiles with the K tiles first, 5-14% and 0-10% slower.
+constexpr int kKmTileK = 64;
+constexpr int kKmTileRows = 64;
+constexpr int kKmThreads = 256;
 
 template <int R, int KA, bool kCachedStore>
-__global__ __launch_bounds__(256) void pack_kmajor_kernel(uint32_t* __restrict__ dst,
-                                                          const uint16_t* __restrict__ src,
-                                                          int64_t rows, int64_t K, int64_t ld) {
-  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile][kTilePitch];
+__global__ __launch_bounds__(kKmThreads) void pack_kmajor_kernel(uint32_t* __restrict__ dst,
+                                                                 const uint16_t* __restrict__ src,
+                                                                 int64_t rows, int64_t K,
+                                                                 int64_t ld) {
+  constexpr int kPitch = kKmTileRows + 8;                         // u16 per LDS row (16-byte aligned)
+  constexpr int kRowChunks = kKmTileRows / 8;                     // 16-byte pieces per k
+  constexpr int kPerLane = kKmTileK * kRowChunks / kKmThreads;    // chunks per lane, each phase
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kKmTileK][kPitch];
   const int tid = threadIdx.x;
-  const int64_t row0 = int64_t(blockIdx.x) * kTile, k0 = int64_t(blockIdx.y) * kTile;
+  const int64_t row0 = int64_t(blockIdx.x) * kKmTileRows, k0 = int64_t(blockIdx.y) * kKmTileK;
   const int64_t b = blockIdx.z;
   const uint16_t* sb = src + b * K * ld;
+  u32x4 v[kPerLane];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = tid + 256 * u;
-    const int kk = c >> 3, rc = (c & 7) * 8;
-    u32x4 v = {0u, 0u, 0u, 0u};
+  for (int u = 0; u < kPerLane; ++u) {
+    const int c = tid + kKmThreads * u;
+    const int kk = c / kRowChunks, rc = (c % kRowChunks) * 8;
+    v[u] = u32x4{0u, 0u, 0u, 0u};
     if (k0 + kk < K && row0 + rc < rows)
-      v = load16_nt(reinterpret_cast<const uint32_t*>(sb + (k0 + kk) * ld + row0 + rc));
-    *reinterpret_cast<u32x4*>(&tile[kk][rc]) = v;
+      v[u] = load16(reinterpret_cast<const uint32_t*>(sb + (k0 + kk) * ld + row0 + rc));
+  }
+#pragma unroll
+  for (int u = 0; u < kPerLane; ++u) {
+    const int c = tid + kKmThreads * u;
+    *reinterpret_cast<u32x4*>(&tile[c / kRowChunks][(c % kRowChunks) * 8]) = v[u];
   }
   __syncthreads();
   constexpr int kLog2R = R == 16 ? 4 : 3;
   const int64_t rows_rep = rows / R, K_rep = K / KA;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int c = tid + 256 * u;
+  for (int u = 0; u < kPerLane; ++u) {
+    const int c = tid + kKmThreads * u;
     // chunk c of the tile: row block c / (8R), then K atom, row in atom, and
     // (KA = 16) half of the atom row
     const int rb = c >> (kLog2R + 3), rem = c & (8 * R - 1);
@@ -205,14 +219,14 @@ __global__ __launch_bounds__(256) void pack_kmajor_kernel(uint32_t* __restrict__
 
 hipError_t launch_pack_kmajor(uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
                               int64_t K, int64_t ld, int R, int atom_k, hipStream_t s) {
-  const dim3 grid(unsigned((rows + kTile - 1) / kTile), unsigned((K + kTile - 1) / kTile),
-                  unsigned(batch));
+  const dim3 grid(unsigned((rows + kKmTileRows - 1) / kKmTileRows),
+                  unsigned((K + kKmTileK - 1) / kKmTileK), unsigned(batch));
   const bool cached = batch * rows * K * 2 <= kCachedPackBytes;
   auto kern = cached ? (R == 16 ? (atom_k == 16 ? pack_kmajor_kernel<16, 16, true> : pack_kmajor_kernel<16, 8, true>)
                                 : (atom_k == 16 ? pack_kmajor_kernel<8, 16, true> : pack_kmajor_kernel<8, 8, true>))
                      : (R == 16 ? (atom_k == 16 ? pack_kmajor_kernel<16, 16, false> : pack_kmajor_kernel<16, 8, false>)
                                 : (atom_k == 16 ? pack_kmajor_kernel<8, 16, false> : pack_kmajor_kernel<8, 8, false>));
-  hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, dst, src, rows, K, ld);
+  hipLaunchKernelGGL(kern, grid, dim3(kKmThreads), 0, s, dst, src, rows, K, ld);
   return hipGetLastError();
 }
 
