@@ -12,6 +12,12 @@ multiply-accumulate from C into D. Prints ONE JSON line on stdout.
 the step's dominant kernel, timed with HIP events on the stream it runs on;
 ``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
 workload on this host's cores.
+
+    python bench.py --op box_copy|box_store|box_reduce_add
+
+times one box transfer instead (a step is one call over the whole box
+workload; ``value`` in GB/s of algorithmic bytes), with the same roofline and
+oracle legs.
 """
 from __future__ import annotations
 
@@ -100,13 +106,122 @@ def cpu_baseline(w, inp, D_gpu, seconds: float, alpha=None, beta=None):
             "sample_matches_gpu": ok}
 
 
+def box_cpu_baseline(bw, op, inp, got, seconds: float):
+    """The oracle's box routine, as it stands, on the first R repeats of the
+    box workload (R sized for about ``seconds`` of CPU time), in GB/s of the
+    same algorithmic bytes; also checks those repeats against the GPU result
+    (``got``: the image for the copy, the tensor after one call from the
+    initial one for the store and the add), bit for bit."""
+    import oracle
+    G0, img = inp["tensor"], inp["image"]
+
+    def run(r):
+        rows = r * bw.box_rows   # the first r boxes lie in these rows
+        t0 = time.perf_counter()
+        if op == "box_copy":
+            out, _ = oracle.box_copy(G0[:rows], bw.box, bw.coords, r, bw.step)
+        else:
+            out, _ = oracle.box_store(G0[:rows], img[:r], bw.box, bw.coords, r, bw.step,
+                                      op="store" if op == "box_store" else "add",
+                                      elem_type=None if op == "box_store" else "f32")
+        return time.perf_counter() - t0, out
+
+    probe = min(8, bw.n_repeat)
+    t_probe, _ = run(probe)
+    r = int(max(probe, min(bw.n_repeat, seconds / max(t_probe, 1e-6) * probe)))
+    t, out = run(r)
+    mine = got[:r] if op == "box_copy" else got[:r * bw.box_rows]
+    ok = bool(np.array_equal(mine.view(np.uint32), out.view(np.uint32)))
+    nbytes = bw.algorithmic_bytes(op) * r / bw.n_repeat
+    return {"value": nbytes / t / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "seconds": round(t, 3),
+            "sample": f"first {r} of {bw.n_repeat} repeats (boxes of {bw.box[0]}x{bw.box[1]} "
+                      f"float32) of workload {bw.name}",
+            "sample_matches_gpu": ok}
+
+
+def run_box(args, torch, bmm):
+    """One step = one box call over the whole workload (every repeat)."""
+    op = args.op
+    name = args.workload or next(iter(workloads.BOX_WORKLOADS))
+    if name not in workloads.BOX_WORKLOADS:
+        raise SystemExit(f"--op {op} needs a box workload: {sorted(workloads.BOX_WORKLOADS)}")
+    bw = workloads.BOX_WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    log(f"[bench] box workload {bw.name}: {bw.n_repeat} boxes of {bw.box} float32, op {op}")
+    inp = workloads.make_box_inputs(bw, seed=0)
+    G0 = torch.from_numpy(inp["tensor"]).to(dev)
+    G = G0.clone()
+    IMG = torch.from_numpy(inp["image"]).to(dev)
+    OUT = torch.empty_like(IMG)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        if op == "box_copy":
+            bmm.box_copy(G, bw.box, bw.coords, bw.n_repeat, bw.step, out=OUT)
+        elif op == "box_store":
+            bmm.box_store(G, IMG, bw.box, bw.coords, bw.n_repeat, bw.step)
+        else:
+            bmm.box_reduce_add(G, IMG, bw.box, bw.coords, "f32", bw.n_repeat, bw.step)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for e in evs:
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    k = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    nbytes = bw.algorithmic_bytes(op)
+    achieved = nbytes / (k.mean() * 1e-3) / 1e9
+    log(f"[bench] {op}: {k.mean()*1e3:.1f} us per call (min {k.min()*1e3:.1f}), "
+        f"{achieved:.0f} GB/s")
+
+    # parity leg: one call from the initial tensor
+    G.copy_(G0)
+    call()
+    torch.cuda.synchronize()
+    got = (OUT if op == "box_copy" else G).cpu().numpy()
+    line = {
+        "metric": f"GB/s of the float32 {op} and % of HBM roofline",
+        "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": bw.name, "op": op, "rows": bw.rows, "cols": bw.cols,
+                   "box": list(bw.box), "n_repeat": bw.n_repeat, "coord_step": list(bw.step),
+                   "swizzle": 0},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic_from_profiles(op, bw.name), "kernel": op,
+                     "avg_launch_us": round(k.mean() * 1e3, 2),
+                     "algorithmic_bytes_per_launch": nbytes},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a sample of the same workload")
+        line["cpu_baseline"] = box_cpu_baseline(bw, op, inp, got, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default=workloads.HEADLINE,
-                    choices=sorted(workloads.WORKLOADS) + sorted(workloads.EXTRA_WORKLOADS))
+    ap.add_argument("--workload", default=None,
+                    choices=sorted(workloads.WORKLOADS) + sorted(workloads.EXTRA_WORKLOADS)
+                    + sorted(workloads.BOX_WORKLOADS),
+                    help=f"default {workloads.HEADLINE} (with --op, the box workload)")
+    ap.add_argument("--op", default="mma", choices=("mma",) + workloads.BOX_OPS,
+                    help="mma: the multiply path (pack A, pack B, mma_tile); box_*: one box "
+                         "transfer over the box workload")
     ap.add_argument("--kernel", default="auto", choices=["auto", "direct", "tiled", "skinny", "tiled128"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -140,7 +255,12 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = {**workloads.WORKLOADS, **workloads.EXTRA_WORKLOADS}[args.workload]
+    if args.op != "mma":
+        run_box(args, torch, bmm)
+        return
+    if args.workload in workloads.BOX_WORKLOADS:
+        ap.error(f"{args.workload} is a box workload: pass --op box_copy|box_store|box_reduce_add")
+    w = {**workloads.WORKLOADS, **workloads.EXTRA_WORKLOADS}[args.workload or workloads.HEADLINE]
     log(f"[bench] workload {w.name}: batch={w.batch} M={w.M} N={w.N} K={w.K} {w.dtype} "
         f"C={'tensor' if w.c_tensor else 'scalar'}")
     inp = workloads.make_inputs(w, seed=0)

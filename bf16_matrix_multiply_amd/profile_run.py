@@ -8,7 +8,9 @@ Run under the profiler (one counter pass per run):
 The driver first runs a plain device-to-device copy of a known size (the
 calibration dispatch: what the counter reads for bytes that are known), then
 ``--reps`` passes of the path (pack A, pack B, multiply-accumulate) on the
-workload's synthetic inputs.
+workload's synthetic inputs; for a box workload, ``--reps`` passes of
+box_copy, box_store and box_reduce_add over it (summarised one at a time with
+``--which box_copy`` and so on).
 
     python3 -m bf16_matrix_multiply_amd.profile_run --summarize FETCH.csv WRITE.csv \
         --workload gemm_8192_bf16_ctensor --kernel mma_tile
@@ -32,9 +34,15 @@ COPY_BYTES = 1 << 30   # calibration copy: 1 GiB read + 1 GiB written
 KERNEL_SOURCES = {
     "mma_tile": ["mma_direct.hip", "mma_tiled.hip", "mma_skinny.hip", "common.h", "launch.h"],
     "pack_operand": ["pack.hip", "common.h"],
+    "box_copy": ["box.hip", "common.h"],
+    "box_store": ["box.hip", "common.h"],
+    "box_reduce_add": ["box.hip", "common.h"],
 }
-# Dispatch-name prefixes of each kernel family (inside the bmm namespace).
-KERNEL_MATCH = {"mma_tile": ("mma_",), "pack_operand": ("pack_kernel<", "pack_staged_kernel<")}
+# Dispatch-name pieces of each kernel family (inside the bmm namespace). The
+# box workloads take the 16-byte path; the add is the float32 one.
+KERNEL_MATCH = {"mma_tile": ("mma_",), "pack_operand": ("pack_kernel<", "pack_staged_kernel<"),
+                "box_copy": ("::box_kernel",), "box_store": ("box_store_kernel_v<0>",),
+                "box_reduce_add": ("box_store_kernel_v<1>",)}
 
 
 def _code_only(text: str) -> str:
@@ -70,6 +78,22 @@ def run(workload: str, reps: int, kernel: str):
     dst.copy_(src)                     # the calibration dispatch
     torch.cuda.synchronize()
     del src, dst
+
+    if workload in workloads.BOX_WORKLOADS:
+        bw = workloads.BOX_WORKLOADS[workload]
+        inp = workloads.make_box_inputs(bw, seed=0)
+        G = torch.from_numpy(inp["tensor"]).to(dev)
+        img = torch.from_numpy(inp["image"]).to(dev)
+        out = torch.empty_like(img)
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            bmm.box_copy(G, bw.box, bw.coords, bw.n_repeat, bw.step, out=out)
+            bmm.box_store(G, img, bw.box, bw.coords, bw.n_repeat, bw.step)
+            bmm.box_reduce_add(G, img, bw.box, bw.coords, "f32", bw.n_repeat, bw.step)
+        torch.cuda.synchronize()
+        print(f"profile_run: copy {COPY_BYTES} B, then {reps} x (box_copy, box_store, "
+              f"box_reduce_add) on {bw.name}", flush=True)
+        return
 
     w = workloads.WORKLOADS[workload]
     inp = workloads.make_inputs(w, seed=0)
@@ -112,7 +136,8 @@ def summarize(fetch_csv, write_csv, workload, kernel):
     sys.path.insert(0, ROOT)
     import workloads
 
-    w = workloads.WORKLOADS[workload]
+    box = workload in workloads.BOX_WORKLOADS
+    w = workloads.BOX_WORKLOADS[workload] if box else workloads.WORKLOADS[workload]
     rec = {"workload": workload, "kernel": kernel, "source_sha": source_sha(kernel),
            "calibration_copy_bytes": COPY_BYTES}
     total = 0.0
@@ -125,7 +150,7 @@ def summarize(fetch_csv, write_csv, workload, kernel):
         mine = [v for i, (n, v) in d.items() if any(m in n for m in KERNEL_MATCH[kernel])]
         # one launch of the multiply per step; packing is two launches per
         # step (A and B), counted together as bench.py's pack roofline does
-        per_step = 1 if kernel == "mma_tile" else 2
+        per_step = 2 if kernel == "pack_operand" else 1
         kib = sum(mine) / (len(mine) / per_step)
         rec[f"{key}_kib_per_dispatch_raw"] = round(kib, 1)
         rec[f"{key}_copy_kib_raw"] = round(copy_kib, 1)
@@ -134,7 +159,9 @@ def summarize(fetch_csv, write_csv, workload, kernel):
         rec[f"{key}_dispatches"] = len(mine)
         total += kib * 1024 * scale
     rec["hbm_bytes_per_launch"] = round(total)
-    if kernel == "mma_tile":
+    if box:
+        rec["algorithmic_bytes_per_launch"] = w.algorithmic_bytes(kernel)
+    elif kernel == "mma_tile":
         rec["algorithmic_bytes_per_launch"] = w.algorithmic_bytes
     else:
         rec["algorithmic_bytes_per_launch"] = 4 * w.batch * (w.M + w.N) * w.K

@@ -166,3 +166,64 @@ def custom(batch, M, N, K, dtype=BF16, a_dist="normal", b_dist="normal", c_tenso
     exact = a_dist == "quarter" and b_dist == "quarter"
     return Workload(name, batch, M, N, K, dtype, a_dist, b_dist, b_scale, c_tensor, c_scalar,
                     exact=exact, c_dist="quarter" if exact else "normal")
+
+
+# ---- box transfers (cp.async.bulk.tensor page: box, coordinates, per-repeat
+# coordinate step, repeat count; "Stores, reductions, and completion" for the
+# store and add directions) ----
+
+@dataclasses.dataclass(frozen=True)
+class BoxWorkload:
+    """A float32 tensor of (rows, cols) moved through rows / box_rows boxes of
+    box_rows x cols, starting at (0, 0) and stepping box_rows rows per repeat:
+    every element of the tensor is in exactly one box."""
+    name: str
+    rows: int
+    cols: int
+    box_rows: int
+
+    @property
+    def n_repeat(self) -> int:
+        return self.rows // self.box_rows
+
+    @property
+    def box(self):
+        return (self.box_rows, self.cols)
+
+    @property
+    def coords(self):
+        return (0, 0)
+
+    @property
+    def step(self):
+        return (self.box_rows, 0)
+
+    @property
+    def image_bytes(self) -> int:
+        return self.n_repeat * self.box_rows * self.cols * 4
+
+    def algorithmic_bytes(self, op: str) -> int:
+        """Each byte touched once: the image and the box region read or written
+        (copy and store: one read, one write; add: two reads, one write)."""
+        return (3 if op == "box_reduce_add" else 2) * self.image_bytes
+
+
+BOX_OPS = ("box_copy", "box_store", "box_reduce_add")
+
+BOX_WORKLOADS = {
+    bw.name: bw
+    for bw in [
+        # 512 MiB in 8192 boxes of 64 x 256 (64 KiB each, the staging limit)
+        BoxWorkload("box_f32_524288x256_64x256", 524288, 256, 64),
+    ]
+}
+
+
+def make_box_inputs(bw: BoxWorkload, seed: int = 0):
+    """Return dict(tensor, image): standard normal float32, drawn in that order;
+    ``image`` is the compact (n_repeat, box_rows, cols) image that the store
+    and add directions write."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((bw.rows, bw.cols), dtype=np.float32)
+    img = rng.standard_normal((bw.n_repeat, bw.box_rows, bw.cols), dtype=np.float32)
+    return dict(tensor=g, image=img)
