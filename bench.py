@@ -45,10 +45,14 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def traffic_from_profiles(kernel: str, workload: str):
+def traffic_from_profiles(kernel: str, workload: str, variant: str = ""):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when there is none or the kernel source changed since it was taken."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    None when there is none or the kernel source changed since it was taken.
+    ``variant`` names what differs from the configuration the plain record
+    was taken in (atom K, the alpha/beta form, split-K, a forced kernel); a
+    variant reports only a record taken for that variant."""
+    tag = f"{kernel}-{variant}" if variant else kernel
+    p = os.path.join(ROOT, "profiles", f"traffic_{tag}_{workload}.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
@@ -382,8 +386,16 @@ def main():
     op_bytes_b = 2 * (w.batch * w.N * w.K * 2)        # pack B: read + write
     mma_s = mm.mean() * 1e-3
     intensity = w.flops / w.algorithmic_bytes
-    times = {"mma_tile": mm.mean(), "pack_operand": pa.mean() + pb.mean()}
+    pack_key = "pack_operand_kmajor" if args.kmajor else "pack_operand"
+    times = {"mma_tile": mm.mean(), pack_key: pa.mean() + pb.mean()}
     dominant = max(times, key=times.get)
+    # what differs from the configuration each kernel's traffic record is taken in
+    pack_variant = "k8" if ka != 16 else ""
+    mma_variant = "+".join(v for v in (
+        "k8" if ka != 16 else "",
+        "scaled" if args.alpha is not None or args.beta is not None else "",
+        f"splitk{splits}" if splits is not None else "",
+        args.kernel if args.kernel != "auto" else "") if v)
     if dominant == "mma_tile":
         if intensity >= RIDGE_FLOP_PER_BYTE:
             achieved, peak, unit, bound = w.flops / mma_s / 1e12, PEAK_MFMA_TFLOPS[w.dtype], \
@@ -397,7 +409,8 @@ def main():
             "GB/s", "hbm"
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4),
-                "traffic": traffic_from_profiles(dominant, w.name),
+                "traffic": traffic_from_profiles(
+                    dominant, w.name, mma_variant if dominant == "mma_tile" else pack_variant),
                 "kernel": dominant if dominant != "mma_tile" else f"mma_tile[{kernel}]",
                 "avg_launch_us": round(times[dominant] * 1e3, 2),
                 "algorithmic_bytes_per_launch": w.algorithmic_bytes if dominant == "mma_tile"

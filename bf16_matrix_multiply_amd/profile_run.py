@@ -34,6 +34,7 @@ COPY_BYTES = 1 << 30   # calibration copy: 1 GiB read + 1 GiB written
 KERNEL_SOURCES = {
     "mma_tile": ["mma_direct.hip", "mma_tiled.hip", "mma_skinny.hip", "common.h", "launch.h"],
     "pack_operand": ["pack.hip", "common.h"],
+    "pack_operand_kmajor": ["pack.hip", "common.h"],
     "box_copy": ["box.hip", "common.h"],
     "box_store": ["box.hip", "common.h"],
     "box_reduce_add": ["box.hip", "common.h"],
@@ -41,6 +42,7 @@ KERNEL_SOURCES = {
 # Dispatch-name pieces of each kernel family (inside the bmm namespace). The
 # box workloads take the 16-byte path; the add is the float32 one.
 KERNEL_MATCH = {"mma_tile": ("mma_",), "pack_operand": ("pack_kernel<", "pack_staged_kernel<"),
+                "pack_operand_kmajor": ("pack_kmajor_kernel<",),
                 "box_copy": ("::box_kernel",), "box_store": ("box_store_kernel_v<0>",),
                 "box_reduce_add": ("box_store_kernel_v<1>",)}
 
@@ -63,7 +65,7 @@ def source_sha(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def run(workload: str, reps: int, kernel: str):
+def run(workload: str, reps: int, kernel: str, kmajor: bool = False):
     sys.path.insert(0, ROOT)
     import numpy as np
     import torch
@@ -99,18 +101,23 @@ def run(workload: str, reps: int, kernel: str):
     inp = workloads.make_inputs(w, seed=0)
     a = torch.from_numpy(inp["a"].view(np.int16)).to(dev)
     b = torch.from_numpy(inp["b"].view(np.int16)).to(dev)
+    if kmajor:   # the operands stored transposed: element (row, k) at [b, k, row]
+        a = a.transpose(1, 2).contiguous()
+        b = b.transpose(1, 2).contiguous()
+    pack = bmm.pack_operand_kmajor if kmajor else bmm.pack_operand
     C = None if inp["c_tensor"] is None else torch.from_numpy(inp["c_tensor"]).to(dev)
-    A = bmm.pack_operand(a, 16)
-    B = bmm.pack_operand(b, 8)
+    A = pack(a, 16)
+    B = pack(b, 8)
     D = torch.empty((w.batch, w.M_rep, w.N_rep, 16, 8), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     for _ in range(reps):
-        bmm.pack_operand(a, 16, out=A)
-        bmm.pack_operand(b, 8, out=B)
+        pack(a, 16, out=A)
+        pack(b, 8, out=B)
         bmm.mma_tile(A, B, C, float(inp["c_scalar"]), w.dtype, out=D, kernel=kernel)
     torch.cuda.synchronize()
-    print(f"profile_run: copy {COPY_BYTES} B, then {reps} x (pack A, pack B, mma_tile[{kernel}]) "
-          f"on {w.name}", flush=True)
+    kind = "K-major " if kmajor else ""
+    print(f"profile_run: copy {COPY_BYTES} B, then {reps} x ({kind}pack A, {kind}pack B, "
+          f"mma_tile[{kernel}]) on {w.name}", flush=True)
 
 
 def _rows(path):
@@ -150,7 +157,7 @@ def summarize(fetch_csv, write_csv, workload, kernel):
         mine = [v for i, (n, v) in d.items() if any(m in n for m in KERNEL_MATCH[kernel])]
         # one launch of the multiply per step; packing is two launches per
         # step (A and B), counted together as bench.py's pack roofline does
-        per_step = 2 if kernel == "pack_operand" else 1
+        per_step = 2 if kernel.startswith("pack_operand") else 1
         kib = sum(mine) / (len(mine) / per_step)
         rec[f"{key}_kib_per_dispatch_raw"] = round(kib, 1)
         rec[f"{key}_copy_kib_raw"] = round(copy_kib, 1)
@@ -174,13 +181,15 @@ def main():
     ap.add_argument("--workload", default="gemm_8192_bf16_ctensor")
     ap.add_argument("--reps", type=int, default=3)
     ap.add_argument("--kernel", default="auto")
+    ap.add_argument("--kmajor", action="store_true",
+                    help="store the operands transposed and pack them with pack_operand_kmajor")
     ap.add_argument("--summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     ap.add_argument("--which", default="mma_tile", choices=sorted(KERNEL_SOURCES))
     args = ap.parse_args()
     if args.summarize:
         print(json.dumps(summarize(*args.summarize, args.workload, args.which), indent=1))
     else:
-        run(args.workload, args.reps, args.kernel)
+        run(args.workload, args.reps, args.kernel, args.kmajor)
 
 
 if __name__ == "__main__":
