@@ -6,6 +6,15 @@
 // tensor, and write the LDS image in the requested XOR-swizzled layout; after a
 // barrier they read the image back through the same swizzle and store it
 // compact and unswizzled.
+//
+// Two paths. When every 16-byte chunk of the box is aligned and wholly inside
+// or outside the tensor (box_chunk_path), each lane moves whole chunks, the
+// swizzle permutes chunks, and the workgroup is sized to the box (up to 1024
+// lanes, at most four chunks each: one round of loads in flight). Otherwise
+// 256 lanes move one element at a time. Since the exported image is the
+// unswizzled one, in both paths a lane reads back exactly the LDS slots it
+// wrote; the swizzled image is the layout a consumer in the same workgroup
+// would read.
 #include "common.h"
 #include "launch.h"
 
