@@ -163,6 +163,9 @@ CHUNK_BOX_CASES = [
     (np.uint8, (3, 80), (2, 48), (1, -16), 3, (1, 48)),
     (np.int64, (9, 12), (3, 4), (-1, -2), 3, (4, 6)),
     (np.uint32, (2, 130, 64), (1, 64, 64), (0, -32, 0), 5, (1, 64, 0)),
+    # 64 KiB boxes (the limit: 1024 lanes, four chunks each)
+    (np.uint32, (300, 300), (64, 256), (-16, 64), 3, (100, 16)),
+    (np.uint8, (400, 304), (256, 256), (-8, 16), 2, (150, 32)),
 ]
 
 

@@ -75,6 +75,9 @@ CHUNK_STORE_CASES = [
     (np.uint64, (9, 12), (3, 4), (-1, -2), 3, (4, 6)),
     (np.uint32, (16, 64), (8, 32), (2, 8), 3, (1, 4)),
     (np.uint16, (12, 64), (4, 32), (-1, 8), 4, (2, -8)),
+    # 64 KiB boxes (the limit), partly outside, the second overlapping its neighbours
+    (np.uint32, (300, 300), (64, 256), (-16, 64), 3, (100, 16)),
+    (np.uint16, (130, 520), (128, 256), (-4, 8), 3, (2, 136)),
 ]
 
 
