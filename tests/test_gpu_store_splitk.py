@@ -256,3 +256,30 @@ def test_splitk_deep_k_sampled():
     assert (np.abs(got - ref) <= gu.BOUND_SCALE * bnd).all()
     got0 = D0[idx[:, 0], idx[:, 1], idx[:, 2]].astype(np.float64)
     assert (np.abs(got - got0) <= 2 * gu.BOUND_SCALE * bnd).all()
+
+
+@pytest.mark.parametrize("splits", [2, 5])
+def test_splitk_reduce_is_the_box_add(splits):
+    """The split-K reduce is the box add reduction fused over the partials:
+    starting from C and applying bmm_box_reduce_add (float32, one rounding per
+    add) to each partial left in the workspace, in split order, gives the
+    split-K result bit for bit (normal data)."""
+    w = C(1, 512, 512, 4096, "bf16", c_tensor=True, name="splitk_box_add")
+    inp = workloads.make_inputs(w, seed=8)
+    A = bmm.pack_operand(gu.dev_u16(inp["a"]), 16)
+    B = bmm.pack_operand(gu.dev_u16(inp["b"]), 8)
+    Cd = torch.from_numpy(inp["c_tensor"]).cuda()
+    ws_bytes = bmm.splitk_workspace_bytes(1, w.M_rep, w.N_rep, w.K_rep, 16, splits)
+    n = w.M * w.N
+    assert ws_bytes == splits * n * 4
+    ws = torch.empty(ws_bytes // 4, dtype=torch.float32, device="cuda")
+    D = bmm.mma_tile_splitk(A, B, Cd, 0.0, "bf16", splits, workspace=ws)
+    rows = n // 256
+    D2 = Cd.clone().view(rows, 256)
+    for s in range(splits):
+        part = ws[s * n:(s + 1) * n].view(rows // 64, 64, 256)
+        bmm.box_reduce_add(D2, part, (64, 256), (0, 0), "f32", rows // 64, (64, 0))
+    torch.cuda.synchronize()
+    got, ref = D.cpu().numpy().reshape(-1), D2.cpu().numpy().reshape(-1)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    gu.assert_parity_full(w, inp, D.cpu().numpy(), f"splitk{splits}")
