@@ -8,8 +8,10 @@ multiply-accumulate from C into D. Prints ONE JSON line on stdout.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--kernel auto]
 
-``value`` is 2*M*N*K*batch / (time per step) in TFLOP/s. ``roofline`` is for
-the step's dominant kernel, timed with HIP events on the stream it runs on;
+``value`` is 2*M*N*K*batch / (time per step) in TFLOP/s, from K steps timed
+as a whole. ``roofline`` is for the step's dominant kernel, timed with HIP
+events on the stream it runs on in a second pass of K steps (an event after
+each kernel: the events cost GPU time, so they stay out of the first pass);
 ``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
 workload on this host's cores.
 
@@ -43,6 +45,27 @@ RIDGE_FLOP_PER_BYTE = 2500e12 / 8000e9
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+MIN_WARMUP_S = 0.1
+
+
+def warm_up(step, n: int, torch) -> int:
+    """Run the n requested warm-up steps, then more until the GPU has been busy
+    for MIN_WARMUP_S: the first few tens of milliseconds of a fresh burst of
+    work run measurably slower (8192^3: 957 against 887-891 us per step after
+    5 warm-up steps). Returns the number of warm-up steps run."""
+    t0 = time.perf_counter()
+    done = 0
+    for _ in range(n):
+        step()
+        done += 1
+    torch.cuda.synchronize()
+    while time.perf_counter() - t0 < MIN_WARMUP_S:
+        step()
+        done += 1
+        torch.cuda.synchronize()
+    return done
 
 
 def traffic_from_profiles(kernel: str, workload: str, variant: str = ""):
@@ -168,19 +191,21 @@ def run_box(args, torch, bmm):
         else:
             bmm.box_reduce_add(G, IMG, bw.box, bw.coords, "f32", bw.n_repeat, bw.step)
 
-    for _ in range(args.warmup):
-        call()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    warmup_run = warm_up(call, args.warmup, torch)
+    # timed region: K calls back to back; then K more, each between two events
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
+    for _ in range(args.steps):
+        call()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     for e in evs:
         e[0].record(stream)
         call()
         e[1].record(stream)
-    end.record(stream)
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
     k = np.array([e[0].elapsed_time(e[1]) for e in evs])
     nbytes = bw.algorithmic_bytes(op)
     achieved = nbytes / (k.mean() * 1e-3) / 1e9
@@ -195,7 +220,8 @@ def run_box(args, torch, bmm):
     line = {
         "metric": f"GB/s of the float32 {op} and % of HBM roofline",
         "value": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": warmup_run,
+        "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": bw.name, "op": op, "rows": bw.rows, "cols": bw.cols,
@@ -217,8 +243,9 @@ def run_box(args, torch, bmm):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="warm-up steps; more run until the GPU has been busy for 100 ms")
     ap.add_argument("--workload", default=None,
                     choices=sorted(workloads.WORKLOADS) + sorted(workloads.EXTRA_WORKLOADS)
                     + sorted(workloads.BOX_WORKLOADS),
@@ -313,26 +340,33 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warmup_run = warm_up(step, args.warmup, torch)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    # The timed region: K whole steps with nothing recorded between the kernels
+    # (a timing event costs the GPU about 3 us, which would land in the step).
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        step()
     end.record(stream)
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
+    # Per-kernel durations: K more steps with an event after each kernel, on the
+    # stream the kernels run on. Each interval includes its closing event.
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
     pa = np.array([e[0].elapsed_time(e[1]) for e in evs])
     pb = np.array([e[1].elapsed_time(e[2]) for e in evs])
     mm = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    evented_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in evs]))
     log(f"[bench] {args.steps} steps: {total_ms:.3f} ms on events, {wall_ms:.3f} ms wall; "
+        f"with per-kernel events {evented_ms * 1e3:.1f} us per step: "
         f"pack A {pa.mean()*1e3:.1f} us, pack B {pb.mean()*1e3:.1f} us, "
         f"mma_tile[{kernel}] {mm.mean()*1e3:.1f} us (min {mm.min()*1e3:.1f})")
 
@@ -418,7 +452,8 @@ def main():
 
     line = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "steps": args.steps, "warmup": args.warmup, "warmup_steps_run": warmup_run,
+        "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
@@ -427,7 +462,9 @@ def main():
                    "step": ("pack_kmajor A + pack_kmajor B + mma_tile" if args.kmajor
                             else "pack A + pack B + mma_tile")},
         "roofline": roofline,
-        "kernels": {"pack_a_us": round(pa.mean() * 1e3, 2), "pack_b_us": round(pb.mean() * 1e3, 2),
+        "kernels": {"timing": "second pass of the K steps, an event after each kernel",
+                    "step_us_with_events": round(evented_ms * 1e3, 2),
+                    "pack_a_us": round(pa.mean() * 1e3, 2), "pack_b_us": round(pb.mean() * 1e3, 2),
                     "mma_tile_us": round(mm.mean() * 1e3, 2),
                     "mma_tile_median_us": round(float(np.median(mm)) * 1e3, 2),
                     "mma_tile_min_us": round(float(mm.min()) * 1e3, 2),
