@@ -247,17 +247,18 @@ int bmm_mma_tile_opts(float* D, const uint32_t* A, const uint32_t* B, const floa
 
 namespace {
 
-// Macro tile of the split-K form: 256 x 256 from 16384 K values, or when
-// there are at least 128 such tiles (then the default count makes tiles x
-// splits fill the chip one workgroup per CU); 128 x 128 otherwise. Measured
-// best-over-splits (us, 256 / 128 tiles): 1024 x 1024 x 8192 37.1 / 32.3,
-// 64 x 8192 x 8192 35.6 / 29.0, 2048 x 2048 x 8192 81.1 / 74.1, 8192 x 1024
-// x 8192 129.6 (2 splits) / 143.6, 3072 x 3072 x 8192 154.9 / 172.6,
-// 2048 x 2048 x 16384 128.3 / 134.1, 1024 x 1024 x 65536 143.4 / 172.9,
-// 512 x 512 x 65536 62.2 / 69.3.
+// Macro tile of the split-K form: 256 x 256 when there are at least 128 such
+// tiles (then the default count makes tiles x splits fill the chip one
+// workgroup per CU), or from 16384 K values when at most 32 splits of them
+// still fill it (8 tiles or more); 128 x 128 otherwise. Measured
+// best-over-splits (us, 256 / 128 tiles): 1024 x 1024 x 8192 36.2 / 31.6,
+// 64 x 8192 x 8192 33.9 / 27.5, 2048 x 2048 x 8192 74.0 / 75.1, 8192 x 1024
+// x 8192 121.3 (2 splits) / 132.5, 3072 x 3072 x 8192 144.5 / 161.2,
+// 2048 x 2048 x 16384 118.5 / 131.2, 1024 x 1024 x 65536 121.0 / 139.2,
+// 512 x 512 x 65536 (4 large tiles) 57.1 / 47.1.
 int splitk_tile(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K) {
   const int64_t tiles256 = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
-  return K >= 16384 || tiles256 >= 128 ? 256 : 128;
+  return tiles256 >= 128 || (K >= 16384 && tiles256 >= 8) ? 256 : 128;
 }
 
 }  // namespace

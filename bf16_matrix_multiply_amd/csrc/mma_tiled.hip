@@ -132,12 +132,17 @@ struct TileCoord {
   int64_t b, mt, nt;
 };
 
-// Linear workgroup id -> (batch, M tile, N tile); a bijection for any count.
-__device__ __forceinline__ TileCoord tile_of(int64_t w, int64_t n_tiles, int64_t MT,
-                                             int64_t NT) {
-  const int64_t q = n_tiles / kXcds, r = n_tiles % kXcds;
+// Linear workgroup id w of n -> linear work index, so that the workgroups one
+// XCD receives (w = xcd, xcd + 8, ...) take a contiguous run of the work; a
+// bijection for any count.
+__device__ __forceinline__ int64_t xcd_run(int64_t w, int64_t n) {
+  const int64_t q = n / kXcds, r = n % kXcds;
   const int64_t xcd = w % kXcds, k = w / kXcds;
-  const int64_t t = xcd * q + (xcd < r ? xcd : r) + k;
+  return xcd * q + (xcd < r ? xcd : r) + k;
+}
+
+// Linear tile index t -> (batch, M tile, N tile), in bands of kGroupM M tiles.
+__device__ __forceinline__ TileCoord tile_at(int64_t t, int64_t MT, int64_t NT) {
   const int64_t per_batch = MT * NT;
   TileCoord c;
   c.b = t / per_batch;
@@ -168,7 +173,15 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / T::kWavesN, wn = wave % T::kWavesN;
-  const TileCoord tc = tile_of(blockIdx.x, n_tiles, MT, NT);
+  // Work item of this workgroup. With splits, the (split, tile) pairs are laid
+  // out split by split and each XCD takes a contiguous run of them, so the
+  // workgroups sharing an XCD's L2 share their K range and most of their A and
+  // B panels (1024 x 1024 x 65536, 16 splits: 2 splits x 16 tiles per XCD,
+  // instead of 2 tiles of every split).
+  const int64_t lin = int64_t(blockIdx.y) * n_tiles + blockIdx.x;
+  const int64_t work = xcd_run(lin, n_tiles * int64_t(p.splits > 1 ? p.splits : 1));
+  const int64_t split = work / n_tiles;
+  const TileCoord tc = tile_at(work % n_tiles, MT, NT);
   const int64_t m_atom0 = tc.mt * kTileMAtoms, n_atom0 = tc.nt * kTileNAtoms;
 
   // ---- direct-to-LDS staging ----
@@ -181,13 +194,13 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
   const int kj = wave & 1;
   const int cs = 2 * kj + (lane >> 5);
   const int64_t nck = k_chunks(p);
-  // Split-K: split s = blockIdx.y sums the 32-value steps
+  // Split-K: split s sums the 32-value steps
   // [s * steps / S, (s + 1) * steps / S) and writes its partial sum to
   // D + s * part_floats; without splits the whole K goes to D.
   int64_t kc0 = 0, kcn = nck;  // first 8-value chunk and chunk count of this split
-  float* const Dout = p.splits > 1 ? p.D + int64_t(blockIdx.y) * p.part_floats : p.D;
+  float* const Dout = p.splits > 1 ? p.D + split * p.part_floats : p.D;
   if (p.splits > 1) {
-    const int64_t sp = blockIdx.y;
+    const int64_t sp = split;
     kc0 = 4 * (sp * p.steps / p.splits);
     const int64_t kc1 = 4 * ((sp + 1) * p.steps / p.splits);
     kcn = (kc1 < nck ? kc1 : nck) - kc0;

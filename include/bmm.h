@@ -356,8 +356,9 @@ int64_t bmm_mma_splitk_workspace_bytes(int64_t batch, int64_t M_rep, int64_t N_r
 
 /* A split count for bmm_mma_tile_splitk: enough tiles x splits for every CU,
  * each split at least 1024 K values deep, at most 32; 1 when splitting does
- * not pay. (The split-K form uses 256 x 256 tiles from K = 16384 values or
- * when there are at least 128 of them, and 128 x 128 tiles otherwise.) */
+ * not pay. (The split-K form uses 256 x 256 tiles when there are at least
+ * 128 of them, or from K = 16384 values when there are at least 8 of them,
+ * and 128 x 128 tiles otherwise.) */
 int bmm_splitk_default(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep,
                        int32_t atom_k);
 

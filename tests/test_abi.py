@@ -357,6 +357,11 @@ def test_splitk_workspace_and_default(L):
     assert L.bmm_splitk_default(1, 128, 256, 1024, 16) == 4
     # 8192 x 1024 x 8192: 128 tiles of 256 x 256 below K = 16384 too, 2 splits
     assert L.bmm_splitk_default(1, 512, 128, 512, 16) == 2
+    # 512 x 512 x 65536: only 4 tiles of 256 x 256, which 32 splits cannot spread
+    # over the chip, so 128 x 128 tiles (16 of them, 16 splits); 1024 x 512 has 8
+    # large tiles, and 32 splits of them
+    assert L.bmm_splitk_default(1, 32, 64, 4096, 16) == 16
+    assert L.bmm_splitk_default(1, 64, 64, 4096, 16) == 32
     # empty problems need no workspace and launch nothing
     assert splitk(L, D=0, A=0, B=0, M=0, ws=0, ws_bytes=0) == 0
 
