@@ -34,7 +34,7 @@ _LIB_PATH = os.path.join(_HERE, "libbmm.so")
 BMM_F16, BMM_BF16 = 0, 1
 _DTYPES = {"f16": BMM_F16, "float16": BMM_F16, torch.float16: BMM_F16,
            "bf16": BMM_BF16, "bfloat16": BMM_BF16, torch.bfloat16: BMM_BF16}
-KERNELS = {"auto": 0, "direct": 1, "tiled": 2, "skinny": 3, "tiled128": 4}
+KERNELS = {"auto": 0, "direct": 1, "tiled": 2, "skinny": 3, "tiled128": 4, "tiled256x128": 5}
 ELEM_TYPES = {"f32": 1, "f16": 2, "bf16": 3, "i32": 4, "i64": 5}
 KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
 

@@ -27,8 +27,9 @@ int hip_status(hipError_t e, const char* what) {
 // Launch-grid limits of the kernels (one workgroup per 256 x 256 tile; the
 // skinny kernel's grid is (N/64, M groups, batch); the direct kernel has one
 // wave per 16 x 16 block, four per workgroup).
-bool tiled_fits(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K, int tile = 256) {
-  const int64_t ma = tile / 16, na = tile / 8;  // M and N atoms per tile
+bool tiled_fits(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K, int tile = 256,
+                int tile_n = 0) {
+  const int64_t ma = tile / 16, na = (tile_n ? tile_n : tile) / 8;  // M and N atoms per tile
   return K < bmm::kTiledMaxK && batch * ((M_rep + ma - 1) / ma) * ((N_rep + na - 1) / na) <= 0x7fffffff;
 }
 bool skinny_fits(int64_t batch, int64_t M_rep, int64_t N_rep) {
@@ -45,6 +46,12 @@ bool direct_fits(int64_t batch, int64_t M_rep, int64_t N_rep) {
 //   tiles leave half the CUs idle while the 512 or fewer small tiles run in one
 //   round at two per CU (8192 x 1024 x 8192, 128 tiles: 144 against 161 us;
 //   2560^3, 100 tiles: 39 against 49 us);
+// - 256 x 128 LDS tiles (the same ping-pong schedule, one workgroup per CU)
+//   when there are more than 128 of them (8192 x 1024 x 8192, 256 tiles: 112.3
+//   against 121.7 us with 128 x 128 tiles; 2304 x 2048 x 4096, 144 tiles: 51.0
+//   against 54.9; 2560^3, 200 tiles: 35.9 against 37.8). With 128 of them the
+//   128 x 128 tile wins (2048 x 2048 x 8192: 80.4 against 71.0 us;
+//   1024 x 4096 x 4096: 44.7 against 39.2);
 // - 128 x 128 LDS tiles when there are at least 128 full ones (2048^3: 24 us
 //   against 40 us with the large tile; 1536^3: 17 against 30 us);
 // - otherwise the K-splitting, B-streaming kernel, fastest or tied for every
@@ -54,8 +61,12 @@ bool direct_fits(int64_t batch, int64_t M_rep, int64_t N_rep) {
 int choose_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K) {
   const int64_t tiles256 = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
   const int64_t tiles128 = batch * ((M_rep + 7) / 8) * ((N_rep + 15) / 16);
+  const int64_t tiles256x128 = batch * ((M_rep + 15) / 16) * ((N_rep + 15) / 16);
   if (M_rep >= 16 && N_rep >= 32 && tiles256 > 128 && tiled_fits(batch, M_rep, N_rep, K))
     return BMM_KERNEL_TILED;
+  if (M_rep >= 16 && N_rep >= 16 && tiles256x128 > 128 &&
+      tiled_fits(batch, M_rep, N_rep, K, 256, 128))
+    return BMM_KERNEL_TILED_256x128;
   if (M_rep >= 8 && N_rep >= 16 && tiles128 >= 128 && tiled_fits(batch, M_rep, N_rep, K, 128))
     return BMM_KERNEL_TILED_128;
   if (skinny_fits(batch, M_rep, N_rep)) return BMM_KERNEL_SKINNY;
@@ -190,18 +201,21 @@ int mma_common(const bmm::MmaArgs& a0, int32_t kernel, void* stream) {
       }
       return hip_status(bmm::launch_mma_direct(a0, s), "mma_tile direct launch");
     case BMM_KERNEL_TILED:
+    case BMM_KERNEL_TILED_256x128:
     case BMM_KERNEL_TILED_128: {
-      const int tile = kernel == BMM_KERNEL_TILED ? 256 : 128;
+      const int tile = kernel == BMM_KERNEL_TILED_128 ? 128 : 256;
+      const int tile_n = kernel == BMM_KERNEL_TILED_256x128 ? 128 : 0;
       if (K >= bmm::kTiledMaxK) {
         g_last_error = "mma_tile: the tiled kernel takes K < 4194304 values";
         return BMM_EINVAL;
       }
-      if (!tiled_fits(a0.batch, a0.M_rep, a0.N_rep, K, tile)) {
+      if (!tiled_fits(a0.batch, a0.M_rep, a0.N_rep, K, tile, tile_n)) {
         g_last_error = "mma_tile: too many macro tiles for one tiled-kernel launch";
         return BMM_EINVAL;
       }
       bmm::MmaArgs a = a0;
       a.tile = tile;
+      a.tile_n = tile_n;
       return hip_status(bmm::launch_mma_tiled(a, s), "mma_tile tiled launch");
     }
     default:

@@ -26,8 +26,10 @@ struct MmaArgs {
   // into that many ranges, partial sums from zero to D + s * part_floats
   int splits;
   int64_t steps, part_floats;
-  // tiled kernel macro tile: 256 (default, also for 0) or 128
+  // tiled kernel macro tile: tile rows 256 (default, also for 0) or 128;
+  // tile_n columns: 0 for as many as rows, or 128 with 256 rows
   int tile;
+  int tile_n;
 };
 
 // In 8-value K chunks, one 32-deep MFMA step spans the same bytes in either

@@ -50,8 +50,10 @@
 // number of barriers. Each barrier is a bare s_barrier after a counted wait,
 // so loads of later slabs stay in flight across it.
 //
-// The 128 x 128 tile (two workgroups per CU, one wave per SIMD each) keeps a
-// one-group schedule: per slab, the MFMAs of the first 16-value half on
+// The 256 x 128 tile runs the same ping-pong schedule with its 8 waves in a
+// 4 x 2 grid of 64 x 64 blocks (three loads per wave per slab). The 128 x 128
+// tile (two workgroups per CU, one wave per SIMD each) keeps a one-group
+// schedule: per slab, the MFMAs of the first 16-value half on
 // fragments already in registers; wait for its own loads of the next slab and
 // its fragment reads; barrier; issue the loads of slab s+4; read the next
 // slab's fragments; the MFMAs of the second half.
@@ -73,25 +75,32 @@
 namespace bmm {
 namespace {
 
-// Macro tile shapes. TM = 256: 8 waves (two per SIMD) in a 2 x 4 grid, each
-// 128 x 64 of D, one workgroup per CU. TM = 128, for problems with too few
-// 256 x 256 tiles to occupy the chip: 4 waves in a 2 x 2 grid, each 64 x 64,
-// a 64 KB ring, two workgroups per CU.
-template <int TM>
+// Macro tile shapes (TM x TN of D):
+// - 256 x 256: 8 waves (two per SIMD) in a 2 x 4 grid, each 128 x 64 of D, one
+//   workgroup per CU;
+// - 256 x 128: 8 waves in a 4 x 2 grid, each 64 x 64, a 96 KB ring, one
+//   workgroup per CU, for problems with too few 256 x 256 tiles to fill the
+//   chip but enough of these;
+// - 128 x 128: 4 waves in a 2 x 2 grid, each 64 x 64, a 64 KB ring, two
+//   workgroups per CU.
+// Every wave covers 64 columns (two 32-column blocks).
+template <int TM, int TN>
 struct Tile {
   static constexpr int kWaves = TM == 256 ? 8 : 4;
-  static constexpr int kWavesN = TM == 256 ? 4 : 2;     // wave grid columns
-  static constexpr int kWaveBlocksM = TM == 256 ? 4 : 2;  // 32-row blocks per wave
+  static constexpr int kWavesN = TN / 64;                 // wave grid columns
+  static constexpr int kWaveBlocksM = TM / 32 / (kWaves / kWavesN);  // 32-row blocks per wave
   static constexpr int kWaveBlocksN = 2;                  // 32-column blocks per wave
   static constexpr int kTileMAtoms = TM / 16;
-  static constexpr int kTileNAtoms = TM / 8;
+  static constexpr int kTileNAtoms = TN / 8;
   static constexpr int kFragsA = TM / 16;   // per slab: TM/32 blocks of 32 rows x 2 K halves
-  static constexpr int kFragsB = TM / 16;   // per slab: TM/32 blocks of 32 columns x 2 K halves
+  static constexpr int kFragsB = TN / 16;   // per slab: TN/32 blocks of 32 columns x 2 K halves
+  // Loads per wave per slab: one per fragment, spread over the waves.
+  static constexpr int kLoadsA = kFragsA / kWaves, kLoadsB = kFragsB / kWaves;
+  static constexpr int kLoadsPerSlab = kLoadsA + kLoadsB;
+  static_assert(kLoadsA * kWaves == kFragsA && kLoadsB * kWaves == kFragsB,
+                "one load per fragment");
+  static_assert(kWaveBlocksM * 32 * (kWaves / kWavesN) == TM, "wave grid covers the tile");
 };
-// Both shapes give every wave one A and one B fragment per 16-value half of a
-// slab: two loads of each operand per slab.
-constexpr int kLoadsA = 2, kLoadsB = 2;
-constexpr int kLoadsPerSlab = kLoadsA + kLoadsB;
 constexpr int kStages = 4;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;
@@ -108,10 +117,10 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
 constexpr int kWaitVmcnt0 = waitcnt_imm(0, 15);
 
 // One ring stage: fragment f of each operand is 64 lanes x 16 bytes.
-template <int TM>
+template <int TM, int TN>
 struct Stage {
-  u32x4 a[Tile<TM>::kFragsA][kWave];
-  u32x4 b[Tile<TM>::kFragsB][kWave];
+  u32x4 a[Tile<TM, TN>::kFragsA][kWave];
+  u32x4 b[Tile<TM, TN>::kFragsB][kWave];
 };
 
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
@@ -156,16 +165,15 @@ __device__ __forceinline__ TileCoord tile_at(int64_t t, int64_t MT, int64_t NT) 
   return c;
 }
 
-template <int TM, int DT, int KA, bool kHasC, bool kScaled>
-__global__ __launch_bounds__(Tile<TM>::kWaves * kWave)
+template <int TM, int TN, int DT, int KA, bool kHasC, bool kScaled>
+__global__ __launch_bounds__((Tile<TM, TN>::kWaves * kWave))
 __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t n_tiles,
                                                               int64_t MT, int64_t NT) {
-  using T = Tile<TM>;
-  using Stage = bmm::Stage<TM>;
+  using T = Tile<TM, TN>;
+  using Stage = bmm::Stage<TM, TN>;
   constexpr int kWaves = T::kWaves, kWaveBlocksM = T::kWaveBlocksM, kWaveBlocksN = T::kWaveBlocksN;
   constexpr int kTileMAtoms = T::kTileMAtoms, kTileNAtoms = T::kTileNAtoms;
-  static_assert(T::kFragsA == kLoadsA * kWaves && T::kFragsB == kLoadsB * kWaves,
-                "one load per fragment");
+  constexpr int kLoadsA = T::kLoadsA, kLoadsB = T::kLoadsB, kLoadsPerSlab = T::kLoadsPerSlab;
   // Four separate objects (not one array) so that the compiler can tell the
   // ring slots apart when it places waits for the direct-to-LDS loads.
   __shared__ __attribute__((aligned(1024))) Stage st0, st1, st2, st3;
@@ -214,7 +222,12 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
   const __amdgpu_buffer_rsrc_t b_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint32_t*>(p.B + (tc.b * p.N_rep + n_atom0) * nck * 32 + kc0 * 32), 0,
       int(b_left < kOutOfRange ? b_left : kOutOfRange), kBufferFlags);
-  uint32_t a_voff[kLoadsA], b_voff[kLoadsB];
+  // Fixed-size arrays: a size that depends on the template arguments, in an
+  // array the lambda below captures, makes the host-side compilation drop the
+  // kernel's launch stub without a diagnostic.
+  constexpr int kMaxLoads = 2;
+  static_assert(kLoadsA <= kMaxLoads && kLoadsB <= kMaxLoads, "offset arrays too small");
+  uint32_t a_voff[kMaxLoads], b_voff[kMaxLoads];
 #pragma unroll
   for (int r = 0; r < kLoadsA; ++r) {
     const int blk = (kWaves * r + wave) >> 1;
@@ -318,7 +331,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
   };
   const int64_t n_slabs = (kcn + 3) / 4;
 
-  if constexpr (TM == 256) {
+  if constexpr (kWaves == 8) {
     // ---- two groups in ping-pong (schedule above) ----
     // All fragments of one slab for this wave: [K half][B blocks, then A blocks].
     u32x4 F[2][kWaveBlocksN + kWaveBlocksM];
@@ -498,9 +511,9 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
       }
 }
 
-template <int TM>
+template <int TM, int TN>
 hipError_t launch_tm(const MmaArgs& a, hipStream_t s) {
-  constexpr int kTileMAtoms = Tile<TM>::kTileMAtoms, kTileNAtoms = Tile<TM>::kTileNAtoms;
+  constexpr int kTileMAtoms = Tile<TM, TN>::kTileMAtoms, kTileNAtoms = Tile<TM, TN>::kTileNAtoms;
   const int64_t MT = (a.M_rep + kTileMAtoms - 1) / kTileMAtoms;
   const int64_t NT = (a.N_rep + kTileNAtoms - 1) / kTileNAtoms;
   const int64_t n_tiles = a.batch * MT * NT;
@@ -510,8 +523,10 @@ hipError_t launch_tm(const MmaArgs& a, hipStream_t s) {
   auto pick = [&](auto dt, auto ka) {
     constexpr int D = decltype(dt)::value, KA = decltype(ka)::value;
     if (a.scaled)
-      return a.C ? mma_tiled_kernel<TM, D, KA, true, true> : mma_tiled_kernel<TM, D, KA, false, true>;
-    return a.C ? mma_tiled_kernel<TM, D, KA, true, false> : mma_tiled_kernel<TM, D, KA, false, false>;
+      return a.C ? mma_tiled_kernel<TM, TN, D, KA, true, true>
+                 : mma_tiled_kernel<TM, TN, D, KA, false, true>;
+    return a.C ? mma_tiled_kernel<TM, TN, D, KA, true, false>
+               : mma_tiled_kernel<TM, TN, D, KA, false, false>;
   };
   auto pick_ka = [&](auto dt) {
     return a.atom_k == 16 ? pick(dt, std::integral_constant<int, 16>{})
@@ -520,15 +535,17 @@ hipError_t launch_tm(const MmaArgs& a, hipStream_t s) {
   auto kern = a.dtype == kBF16 ? pick_ka(std::integral_constant<int, kBF16>{})
                                : pick_ka(std::integral_constant<int, kF16>{});
   const unsigned splits = a.splits > 1 ? unsigned(a.splits) : 1u;
-  hipLaunchKernelGGL(kern, dim3(unsigned(n_tiles), splits), dim3(Tile<TM>::kWaves * kWave), 0, s,
-                     a, n_tiles, MT, NT);
+  constexpr unsigned kThreads = Tile<TM, TN>::kWaves * kWave;  // (no comma inside the macro)
+  hipLaunchKernelGGL(kern, dim3(unsigned(n_tiles), splits), dim3(kThreads), 0, s, a, n_tiles, MT,
+                     NT);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_mma_tiled(const MmaArgs& a, hipStream_t s) {
-  return a.tile == 128 ? launch_tm<128>(a, s) : launch_tm<256>(a, s);
+  if (a.tile == 128) return launch_tm<128, 128>(a, s);
+  return a.tile_n == 128 ? launch_tm<256, 128>(a, s) : launch_tm<256, 256>(a, s);
 }
 
 }  // namespace bmm

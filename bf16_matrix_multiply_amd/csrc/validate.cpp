@@ -219,7 +219,7 @@ Status check_mma(const float* D, const uint32_t* A, const uint32_t* B, const flo
     return fail(BMM_EINVAL, "mma_tile: atom_k must be 16 or 8, got %lld", atom_k);
   if (dtype != BMM_F16 && dtype != BMM_BF16)
     return fail(BMM_EINVAL, "mma_tile: dtype %lld is neither BMM_F16 nor BMM_BF16", dtype);
-  if (kernel < BMM_KERNEL_AUTO || kernel > BMM_KERNEL_TILED_128)
+  if (kernel < BMM_KERNEL_AUTO || kernel > BMM_KERNEL_TILED_256x128)
     return fail(BMM_EINVAL, "mma_tile: unknown kernel %lld", kernel);
   if (batch < 0 || M_rep < 0 || N_rep < 0 || K_rep < 0)
     return fail(BMM_EINVAL, "mma_tile: negative extent");

@@ -21,7 +21,9 @@ DEFAULT_SHAPES = [(128, 128, 256), (512, 512, 512), (1024, 1024, 1024), (1536, 1
                   (4096, 4096, 4096), (8192, 8192, 8192), (1024, 1024, 8192), (2048, 2048, 8192),
                   (1024, 4096, 4096), (2048, 1024, 4096), (1024, 1024, 65536), (512, 512, 65536),
                   (16, 1024, 1024), (64, 2048, 2048), (256, 4096, 4096), (512, 2048, 2048),
-                  (64, 8192, 8192), (32, 16384, 4096), (16, 16384, 16384)]
+                  (64, 8192, 8192), (32, 16384, 4096), (16, 16384, 16384),
+                  (8192, 1024, 8192), (1024, 8192, 8192), (2304, 2304, 4096), (3072, 2048, 4096),
+                  (2816, 2816, 4096)]
 
 
 def _median_us(fn, reps=8):
@@ -46,7 +48,7 @@ def sweep(shapes):
         A, B = bmm.pack_operand(a, 16), bmm.pack_operand(b, 8)
         D = torch.empty(1, M // 16, N // 8, 16, 8, device=dev)
         times = {}
-        for k in ("direct", "tiled", "tiled128", "skinny"):
+        for k in ("direct", "tiled", "tiled256x128", "tiled128", "skinny"):
             times[k] = _median_us(lambda: bmm.mma_tile(A, B, None, 0.0, "bf16", out=D, kernel=k))
         auto = bmm.select_kernel(1, M // 16, N // 8, K // 16)
         default = bmm.splitk_default(1, M // 16, N // 8, K // 16)

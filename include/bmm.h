@@ -44,16 +44,18 @@ enum {
 };
 
 /* Kernel selection for bmm_mma_tile_with. AUTO picks by shape (TILED with
- * more than 128 256 x 256 tiles, ragged ones counted, else TILED_128 with at
- * least 128 128 x 128 tiles, else SKINNY, else DIRECT if a grid limit rules
- * the others out); the others force one kernel (every kernel accepts every
- * valid shape within its launch-grid limits). */
+ * more than 128 256 x 256 tiles, ragged ones counted, else TILED_256x128 with
+ * more than 128 256 x 128 tiles, else TILED_128 with at least 128 128 x 128
+ * tiles, else SKINNY, else DIRECT if a grid limit rules the others out); the
+ * others force one kernel (every kernel accepts every valid shape within its
+ * launch-grid limits). All three tiled kernels give identical results. */
 typedef enum {
   BMM_KERNEL_AUTO = 0,
   BMM_KERNEL_DIRECT = 1, /* one wave per 16x16 output block, operands straight from HBM */
   BMM_KERNEL_TILED = 2,  /* LDS-staged 256x256 macro tiles for large M and N */
   BMM_KERNEL_SKINNY = 3, /* few output tiles: K split across the waves of a workgroup, B streamed */
-  BMM_KERNEL_TILED_128 = 4 /* LDS-staged 128x128 macro tiles, two workgroups per CU */
+  BMM_KERNEL_TILED_128 = 4, /* LDS-staged 128x128 macro tiles, two workgroups per CU */
+  BMM_KERNEL_TILED_256x128 = 5 /* LDS-staged 256 (M) x 128 (N) macro tiles, one per CU */
 } bmm_kernel;
 
 /*

@@ -163,14 +163,20 @@ def test_plain_entry_point_validates(L):
 
 def test_select_kernel(L):
     assert L.bmm_select_kernel(-1, 1, 1, 1) == EINVAL
-    # 256 x 256 tiles only above 128 of them: 8192 x 1024 (128 tiles) takes
-    # 128 x 128 tiles, 3072^3 (144 tiles) and 8192^3 the large ones
-    assert L.bmm_select_kernel(1, 512, 128, 512) == 4
+    # 256 x 256 tiles only above 128 of them: 3072^3 (144 tiles) and 8192^3
+    # take the large ones; 8192 x 1024 (128 of them) takes 256 x 128 tiles (256
+    # of those), as do 2560^2 (200) and 2304 x 2048 (144); 2048^2 (128 of
+    # those) takes 128 x 128
+    assert L.bmm_select_kernel(1, 512, 128, 512) == 5
+    assert L.bmm_select_kernel(1, 64, 1024, 512) == 5
+    assert L.bmm_select_kernel(1, 160, 320, 256) == 5
+    assert L.bmm_select_kernel(1, 144, 256, 256) == 5
+    assert L.bmm_select_kernel(1, 128, 256, 512) == 4
     assert L.bmm_select_kernel(1, 192, 384, 192) == 2
     assert L.bmm_select_kernel(1, 512, 1024, 512) == 2
     for shape in [(1, 1, 1, 2), (1, 8, 16, 16), (1, 256, 512, 256), (1, 1, 2048, 1024),
                   (1, 512, 1024, 512)]:
-        assert L.bmm_select_kernel(*shape) in (1, 2, 3, 4)
+        assert L.bmm_select_kernel(*shape) in (1, 2, 3, 4, 5)
 
 
 def pack_km(L, dst=P0, src=P1, batch=1, rows=16, K=32, ld=16, R=16):

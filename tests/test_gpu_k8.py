@@ -20,7 +20,7 @@ from tests import util
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = ["direct", "tiled", "skinny", "tiled128"]
+KERNELS = ["direct", "tiled", "skinny", "tiled128", "tiled256x128"]
 C = workloads.custom
 
 CASES = {

@@ -17,7 +17,7 @@ from tests import util
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = ["direct", "tiled", "skinny", "tiled128"]
+KERNELS = ["direct", "tiled", "skinny", "tiled128", "tiled256x128"]
 
 C = workloads.custom
 SMALL = {
@@ -226,9 +226,9 @@ def test_mid_size_tiled128_sampled(shape, kernel):
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_tile_shapes_bitwise(dtype):
-    """Normal data, ragged M and N, an odd K_rep: the 256 x 256 and the
-    128 x 128 tile each give every 32 x 32 block of D the C value first and
-    then one 32x32x16 MFMA per K atom pair in ascending K, so the two agree
+    """Normal data, ragged M and N, an odd K_rep: the 256 x 256, 256 x 128 and
+    128 x 128 tiles each give every 32 x 32 block of D the C value first and
+    then one 32x32x16 MFMA per K atom pair in ascending K, so the three agree
     bit for bit. The split-K form with a single split forms the partial sum
     from zero and then adds C once, so it gives fl(C + P) with P the product
     that either tile gives for a scalar C of 0."""
@@ -236,7 +236,9 @@ def test_tile_shapes_bitwise(dtype):
     inp = workloads.make_inputs(w, seed=6)
     A, B, Cd, D256 = gu.gpu_run(w, inp, "tiled")
     _, _, _, D128 = gu.gpu_run(w, inp, "tiled128")
+    _, _, _, D2561 = gu.gpu_run(w, inp, "tiled256x128")
     assert np.array_equal(D256.view(np.uint32), D128.view(np.uint32))
+    assert np.array_equal(D256.view(np.uint32), D2561.view(np.uint32))
     gu.assert_parity_full(w, inp, D256, "tiled")
     P = {k: bmm.mma_tile(A, B, None, 0.0, dtype, kernel=k).cpu().numpy()
          for k in ("tiled", "tiled128")}

@@ -19,7 +19,7 @@ from tests import gpu_util as gu
 
 pytestmark = pytest.mark.gpu
 
-KERNELS = ["direct", "tiled", "skinny", "tiled128"]
+KERNELS = ["direct", "tiled", "skinny", "tiled128", "tiled256x128"]
 
 
 def _cases():
