@@ -253,7 +253,8 @@ def main():
     ap.add_argument("--op", default="mma", choices=("mma",) + workloads.BOX_OPS,
                     help="mma: the multiply path (pack A, pack B, mma_tile); box_*: one box "
                          "transfer over the box workload")
-    ap.add_argument("--kernel", default="auto", choices=["auto", "direct", "tiled", "skinny", "tiled128"])
+    ap.add_argument("--kernel", default="auto",
+                    choices=["auto", "direct", "tiled", "skinny", "tiled128", "tiled256x128"])
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--alpha", type=float, default=None,
