@@ -61,3 +61,19 @@ def test_box_workload_bytes():
     assert bw.n_repeat == 8192 and bw.image_bytes == 512 << 20
     assert bw.algorithmic_bytes("box_copy") == bw.algorithmic_bytes("box_store") == 1 << 30
     assert bw.algorithmic_bytes("box_reduce_add") == 3 * (512 << 20)
+
+
+def test_traffic_records_per_configuration():
+    """A traffic record applies to the configuration it was taken in: the plain
+    k = 16 multiply at 8192^3 has one (and it is current), a variant such as
+    the alpha/beta form or split-K reports none."""
+    import json
+    from bf16_matrix_multiply_amd.profile_run import source_sha
+    rec = json.load(open(os.path.join(ROOT, "profiles",
+                                      "traffic_mma_tile_gemm_8192_bf16_ctensor.json")))
+    assert rec["source_sha"] == source_sha("mma_tile")
+    got = bench.traffic_from_profiles("mma_tile", "gemm_8192_bf16_ctensor")
+    assert got == rec["hbm_bytes_per_launch"] and got > rec["algorithmic_bytes_per_launch"]
+    for variant in ("scaled", "k8", "splitk2", "tiled128"):
+        assert bench.traffic_from_profiles("mma_tile", "gemm_8192_bf16_ctensor", variant) is None
+    assert bench.traffic_from_profiles("pack_operand_kmajor", "gemm_8192_bf16_ctensor") > 0
