@@ -41,19 +41,19 @@ bool direct_fits(int64_t batch, int64_t M_rep, int64_t N_rep) {
 
 // Shape rule of BMM_KERNEL_AUTO (K counted in values), from a sweep of the
 // kernels over shapes from 16 x 1024 x 1024 to 8192^3 on MI355X:
-// - 256 x 256 LDS tiles when there are more than 128 (3072^3, 144 tiles: 61
-//   us against 69 us with 128 x 128 tiles). With 128 or fewer, the large
-//   tiles leave half the CUs idle while the 512 or fewer small tiles run in one
-//   round at two per CU (8192 x 1024 x 8192, 128 tiles: 144 against 161 us;
-//   2560^3, 100 tiles: 39 against 49 us);
+// - 256 x 256 LDS tiles when there are more than 128 (3072^3, 144 tiles:
+//   59.6 us against 67.2 with 128 x 128 tiles and 73.7 with 256 x 128). With
+//   128 or fewer the large tiles leave half the CUs idle (8192 x 1024 x 8192,
+//   128 tiles: 134.7 us);
 // - 256 x 128 LDS tiles (the same ping-pong schedule, one workgroup per CU)
 //   when there are more than 128 of them (8192 x 1024 x 8192, 256 tiles: 112.3
 //   against 121.7 us with 128 x 128 tiles; 2304 x 2048 x 4096, 144 tiles: 51.0
 //   against 54.9; 2560^3, 200 tiles: 35.9 against 37.8). With 128 of them the
 //   128 x 128 tile wins (2048 x 2048 x 8192: 80.4 against 71.0 us;
 //   1024 x 4096 x 4096: 44.7 against 39.2);
-// - 128 x 128 LDS tiles when there are at least 128 full ones (2048^3: 24 us
-//   against 40 us with the large tile; 1536^3: 17 against 30 us);
+// - 128 x 128 LDS tiles when there are at least 128 full ones (2048^3: 24.2
+//   us against 28.0 with 256 x 128 and 38.8 with 256 x 256; 1536^3: 18.2
+//   against 21.3 and 31.5);
 // - otherwise the K-splitting, B-streaming kernel, fastest or tied for every
 //   shape with fewer tiles (1024 x 1024 x 8192: 41 against 58 us;
 //   256 x 4096 x 4096: 24 against 33 us);
