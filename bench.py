@@ -68,7 +68,7 @@ def warm_up(step, n: int, torch) -> int:
     return done
 
 
-def traffic_from_profiles(kernel: str, workload: str, variant: str = ""):
+def traffic_from_profiles(kernel: str, workload: str, variant: str = "", mma_kernel=None):
     """HBM bytes per launch from the committed rocprofv3 counter summary, or
     None when there is none or the kernel source changed since it was taken.
     ``variant`` names what differs from the configuration the plain record
@@ -81,6 +81,10 @@ def traffic_from_profiles(kernel: str, workload: str, variant: str = ""):
     rec = json.load(open(p))
     if rec.get("source_sha") != source_sha(kernel):
         log(f"traffic record {p} is stale (kernel source changed); reporting null")
+        return None
+    if mma_kernel is not None and rec.get("mma_kernel") not in (None, mma_kernel):
+        log(f"traffic record {p} was taken with {rec['mma_kernel']}, not {mma_kernel}; "
+            "reporting null")
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -445,7 +449,8 @@ def main():
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4),
                 "traffic": traffic_from_profiles(
-                    dominant, w.name, mma_variant if dominant == "mma_tile" else pack_variant),
+                    dominant, w.name, mma_variant if dominant == "mma_tile" else pack_variant,
+                    kernel if dominant == "mma_tile" else None),
                 "kernel": dominant if dominant != "mma_tile" else f"mma_tile[{kernel}]",
                 "avg_launch_us": round(times[dominant] * 1e3, 2),
                 "algorithmic_bytes_per_launch": w.algorithmic_bytes if dominant == "mma_tile"

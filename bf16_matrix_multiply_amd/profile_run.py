@@ -97,7 +97,7 @@ def run(workload: str, reps: int, kernel: str, kmajor: bool = False):
               f"box_reduce_add) on {bw.name}", flush=True)
         return
 
-    w = workloads.WORKLOADS[workload]
+    w = {**workloads.WORKLOADS, **workloads.EXTRA_WORKLOADS}[workload]
     inp = workloads.make_inputs(w, seed=0)
     a = torch.from_numpy(inp["a"].view(np.int16)).to(dev)
     b = torch.from_numpy(inp["b"].view(np.int16)).to(dev)
@@ -144,7 +144,7 @@ def summarize(fetch_csv, write_csv, workload, kernel):
     import workloads
 
     box = workload in workloads.BOX_WORKLOADS
-    w = workloads.BOX_WORKLOADS[workload] if box else workloads.WORKLOADS[workload]
+    w = workloads.BOX_WORKLOADS[workload] if box else {**workloads.WORKLOADS, **workloads.EXTRA_WORKLOADS}[workload]
     rec = {"workload": workload, "kernel": kernel, "source_sha": source_sha(kernel),
            "calibration_copy_bytes": COPY_BYTES}
     total = 0.0
@@ -170,6 +170,9 @@ def summarize(fetch_csv, write_csv, workload, kernel):
         rec["algorithmic_bytes_per_launch"] = w.algorithmic_bytes(kernel)
     elif kernel == "mma_tile":
         rec["algorithmic_bytes_per_launch"] = w.algorithmic_bytes
+        # the kernel AUTO ran (the run uses --kernel auto): a record holds for it only
+        import bf16_matrix_multiply_amd as bmm
+        rec["mma_kernel"] = bmm.select_kernel(w.batch, w.M_rep, w.N_rep, w.K_rep)
     else:
         rec["algorithmic_bytes_per_launch"] = 4 * w.batch * (w.M + w.N) * w.K
     rec["traffic_over_algorithmic"] = round(total / rec["algorithmic_bytes_per_launch"], 3)

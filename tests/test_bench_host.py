@@ -76,4 +76,8 @@ def test_traffic_records_per_configuration():
     assert got == rec["hbm_bytes_per_launch"] and got > rec["algorithmic_bytes_per_launch"]
     for variant in ("scaled", "k8", "splitk2", "tiled128"):
         assert bench.traffic_from_profiles("mma_tile", "gemm_8192_bf16_ctensor", variant) is None
+    # a multiply record holds only for the kernel it was taken with
+    assert rec["mma_kernel"] == "tiled"
+    assert bench.traffic_from_profiles("mma_tile", "gemm_8192_bf16_ctensor", "", "tiled") == got
+    assert bench.traffic_from_profiles("mma_tile", "gemm_8192_bf16_ctensor", "", "skinny") is None
     assert bench.traffic_from_profiles("pack_operand_kmajor", "gemm_8192_bf16_ctensor") > 0
