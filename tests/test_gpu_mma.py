@@ -192,6 +192,19 @@ def test_full_gemm_8192_bf16_ctensor():
     gu.assert_parity_sampled(w, inp, D)
 
 
+@pytest.mark.parametrize("name", ["shard_n8_8192x1024x8192_bf16_ctensor",
+                                  "shard_m8_1024x8192x8192_bf16_ctensor"])
+def test_full_shard_256x128_sampled(name):
+    """One GPU's share of an 8-way split of the 8192^3 workload, at its real
+    shape: AUTO runs the 256 x 128 tile there (256 tiles), sampled outputs
+    within bound."""
+    w = workloads.EXTRA_WORKLOADS[name]
+    assert bmm.select_kernel(w.batch, w.M_rep, w.N_rep, w.K_rep) == "tiled256x128"
+    inp = workloads.make_inputs(w, seed=0)
+    _, _, _, D = gu.gpu_run(w, inp)
+    gu.assert_parity_sampled(w, inp, D)
+
+
 @pytest.mark.parametrize("name", ["skinny_16x16384x16384_bf16", "gemm_8192_bf16_ctensor"])
 def test_full_quantised_variants(name):
     """The large bf16 shapes with quarter-integer operands: bit-exact samples
