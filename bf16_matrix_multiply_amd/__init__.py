@@ -121,6 +121,18 @@ def lib():
     return _lib
 
 
+def _dtype_code(dtype, fn: str) -> int:
+    """The C ABI's element type for ``dtype``. Packed words carry no type, so the
+    caller must name it: a missing or unknown dtype is an error, never a default
+    (the tile operation changes no input type)."""
+    if dtype is None:
+        raise ValueError(f"{fn}: dtype is required ('f16' or 'bf16'): packed words carry no type")
+    try:
+        return _DTYPES[dtype]
+    except (KeyError, TypeError):
+        raise ValueError(f"{fn}: unknown dtype {dtype!r}; expected 'f16' or 'bf16'") from None
+
+
 def _check(rc: int):
     if rc < 0:
         raise BmmError(rc, lib().bmm_last_error().decode())
@@ -277,13 +289,15 @@ def splitk_default(batch, M_rep, N_rep, K_rep, atom_k=16) -> int:
 
 
 def mma_tile_splitk(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None,
-                    c: float = 0.0, dtype="bf16", splits: int | None = None,
+                    c: float = 0.0, dtype=None, splits: int | None = None,
                     out: torch.Tensor | None = None,
                     workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Split-K form: D = (((C + P_0) + P_1) + ...), P_s the partial sums of
     balanced ranges of 32-value K steps (bmm_mma_tile_splitk). ``splits``
     defaults to bmm_splitk_default; ``workspace`` (float32, at least
-    bmm_mma_splitk_workspace_bytes) is allocated here when not given."""
+    bmm_mma_splitk_workspace_bytes) is allocated here when not given. ``dtype``
+    ('f16' or 'bf16') is required."""
+    dt = _dtype_code(dtype, "mma_tile_splitk")
     _require_cuda(A, B, C, out, workspace)
     if A.dim() != 5 or B.dim() != 5 or A.shape[3] != 16 or B.shape[3] != 8 or \
             A.shape[4] not in (8, 4) or B.shape[4] != A.shape[4]:
@@ -314,13 +328,13 @@ def mma_tile_splitk(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = N
         raise ValueError("mma_tile_splitk: workspace must be contiguous")
     ws_bytes = workspace.numel() * workspace.element_size()
     _check(lib().bmm_mma_tile_splitk(_ptr(out), _ptr(A), _ptr(B), _ptr(C), float(c), batch, M_rep,
-                                     N_rep, K_rep, _DTYPES[dtype], atom_k, splits,
+                                     N_rep, K_rep, dt, atom_k, splits,
                                      _ptr(workspace), ws_bytes, _stream(A)))
     return out
 
 
 def mma_tile(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None,
-             c: float = 0.0, dtype="bf16", out: torch.Tensor | None = None,
+             c: float = 0.0, dtype=None, out: torch.Tensor | None = None,
              kernel: str = "auto", alpha: float | None = None,
              beta: float | None = None) -> torch.Tensor:
     """D = A * B^T + C over packed operands; returns D (batch, M/16, N/8, 16, 8).
@@ -330,7 +344,9 @@ def mma_tile(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None,
     beta given, the alpha/beta form runs instead (bmm_mma_tile_scaled):
     D = fma(alpha, A * B^T, beta * C), the product accumulated from zero.
     Operands packed with an atom K of 8 ((..., 16, 4) and (..., 8, 4) words)
-    go through bmm_mma_tile_opts with atom_k = 8."""
+    go through bmm_mma_tile_opts with atom_k = 8. ``dtype`` ('f16' or 'bf16',
+    the type both operands were packed from) is required."""
+    dt = _dtype_code(dtype, "mma_tile")
     _require_cuda(A, B, C, out)
     if A.dim() != 5 or B.dim() != 5 or A.shape[3] != 16 or B.shape[3] != 8 or \
             A.shape[4] not in (8, 4) or B.shape[4] != A.shape[4]:
@@ -357,16 +373,16 @@ def mma_tile(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None,
         opts = MmaOpts(8, KERNELS[kernel], int(scaled), 1.0 if alpha is None else float(alpha),
                        1.0 if beta is None else float(beta))
         _check(lib().bmm_mma_tile_opts(_ptr(out), _ptr(A), _ptr(B), _ptr(C), float(c), batch,
-                                       M_rep, N_rep, K_rep, _DTYPES[dtype], ctypes.byref(opts),
+                                       M_rep, N_rep, K_rep, dt, ctypes.byref(opts),
                                        _stream(A)))
     elif alpha is None and beta is None:
         _check(lib().bmm_mma_tile_with(_ptr(out), _ptr(A), _ptr(B), _ptr(C), float(c), batch,
-                                       M_rep, N_rep, K_rep, _DTYPES[dtype], KERNELS[kernel],
+                                       M_rep, N_rep, K_rep, dt, KERNELS[kernel],
                                        _stream(A)))
     else:
         _check(lib().bmm_mma_tile_scaled(
             _ptr(out), _ptr(A), _ptr(B), _ptr(C), float(c), 1.0 if alpha is None else float(alpha),
-            1.0 if beta is None else float(beta), batch, M_rep, N_rep, K_rep, _DTYPES[dtype],
+            1.0 if beta is None else float(beta), batch, M_rep, N_rep, K_rep, dt,
             KERNELS[kernel], _stream(A)))
     return out
 

@@ -17,7 +17,6 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbmm.so")
-MICROBENCH = os.path.join(HERE, "microbench")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
@@ -68,19 +67,7 @@ def build(verbose: bool = False) -> str:
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
           *[o for _, o in jobs]])
     os.replace(tmp, LIB)
-    build_microbench()
     return LIB
-
-
-def build_microbench() -> list[str]:
-    """Chip probes (stand-alone executables, not part of the library)."""
-    out = []
-    for f in sorted(os.listdir(MICROBENCH)):
-        if f.endswith(".hip"):
-            exe = os.path.join(MICROBENCH, f[:-4])
-            _run([HIPCC, *HIP_FLAGS, os.path.join(MICROBENCH, f), "-o", exe])
-            out.append(exe)
-    return out
 
 
 if __name__ == "__main__":

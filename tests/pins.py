@@ -295,6 +295,54 @@ def pin_sampled_matches_full(o):
     assert np.array_equal(got, full[idx[:, 0], idx[:, 1], idx[:, 2]])
 
 
+def pin_bound(o):
+    """The tolerance scale of every normal-input parity test, |A|.|B|^T + |C|
+    (absolute values elementwise), against float64 numpy on the decoded
+    absolute values of the same halves: a sum of non-negative terms, so the
+    oracle's fp32 recurrence lies within gamma_K of it relatively. Words whose
+    two halves differ only in the sign bit, a C tensor of both signs and a
+    negative scalar c are included; the sampled form equals the full form."""
+    rng = np.random.default_rng(11)
+    for dt, (batch, Mr, Nr, Kr) in (("bf16", (2, 2, 3, 5)), ("f16", (1, 3, 2, 4))):
+        M, N, K = 16 * Mr, 8 * Nr, 16 * Kr
+        a = workloads.draw_operand(rng, "normal", (batch, M, K), dt)
+        b = workloads.draw_operand(rng, "normal", (batch, N, K), dt)
+        # first atom row of A: each word holds x and -x (halves differing in sign only)
+        a[:, :16, 1::2] = a[:, :16, 0::2] ^ np.uint16(0x8000)
+        C = rng.standard_normal((batch, Mr, Nr, 16, 8), dtype=np.float32)
+        A, B = o.pack(a, 16), o.pack(b, 8)
+        af, bf = np.abs(util.decode(a, dt)), np.abs(util.decode(b, dt))
+        prod = af @ bf.transpose(0, 2, 1)
+        for Ct, c in ((C, 0.0), (None, -0.75)):
+            ref = prod + (np.abs(util.tile_to_logical(Ct).astype(np.float64)) if Ct is not None
+                          else abs(c))
+            got = util.tile_to_logical(o.bound(A, B, Ct, c, dt)).astype(np.float64)
+            assert (got >= 0).all(), dt
+            assert (np.abs(got - ref) <= util.gamma(K) * ref).all(), \
+                (dt, c, float((np.abs(got - ref) / ref).max()))
+            idx = util.sample_indices(rng, batch, M, N, 100)
+            assert np.array_equal(o.bound(A, B, Ct, c, dt, idx),
+                                  util.tile_to_logical(o.bound(A, B, Ct, c, dt))[
+                                      idx[:, 0], idx[:, 1], idx[:, 2]]), (dt, "sampled")
+
+
+def pin_k8_sampled_matches_full(o):
+    """The sampled entry of the k = 8 form (the reference of the full-size
+    k = 8 tests) returns exactly the full k = 8 result's elements, with a C
+    tensor and with a scalar c, for an odd number of k = 8 atoms."""
+    rng = np.random.default_rng(12)
+    dt, batch, Mr, Nr, K = "bf16", 2, 2, 3, 8 * 7
+    M, N = 16 * Mr, 8 * Nr
+    A = o.pack_k8(workloads.draw_operand(rng, "normal", (batch, M, K), dt), 16)
+    B = o.pack_k8(workloads.draw_operand(rng, "normal", (batch, N, K), dt), 8)
+    C = rng.standard_normal((batch, Mr, Nr, 16, 8), dtype=np.float32)
+    idx = util.sample_indices(rng, batch, M, N, 150)
+    for Ct, c in ((C, 0.0), (None, -0.5)):
+        full = util.tile_to_logical(o.mma_k8(A, B, Ct, c, dt))
+        got = o.mma_k8_sampled(A, B, Ct, c, dt, idx)
+        assert np.array_equal(got, full[idx[:, 0], idx[:, 1], idx[:, 2]]), c
+
+
 def pin_box_page_example(o):
     """The page's two-box example: the (2,8,16) image read back row by row is
     arange(256); 512 bytes per box, 1024 per barrier phase."""

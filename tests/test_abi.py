@@ -379,3 +379,20 @@ def test_kernel_grid_limits(L):
     assert L.bmm_select_kernel(70000, 4, 2048, 1024) != 3
     # forcing a kernel past its grid limit is a clear EINVAL, nothing launched
     assert mma(L, batch=70000, M=1, N=1, K=1, kernel=3) == EINVAL and "skinny" in err(L)
+
+
+@pytest.mark.parametrize("fn", ["mma_tile", "mma_tile_splitk"])
+def test_binding_requires_dtype(fn):
+    """Packed words carry no element type, so the binding takes no default: a
+    call without dtype, or with an unknown one, is refused before any library
+    call (the tile operation changes no input type)."""
+    import torch
+    A = torch.zeros((1, 1, 2, 16, 8), dtype=torch.int32)
+    B = torch.zeros((1, 1, 2, 8, 8), dtype=torch.int32)
+    f = getattr(bmm, fn)
+    with pytest.raises(ValueError, match="dtype is required"):
+        f(A, B)
+    with pytest.raises(ValueError, match="dtype is required"):
+        f(A, B, None, 0.0)
+    with pytest.raises(ValueError, match="unknown dtype"):
+        f(A, B, None, 0.0, "fp8")

@@ -1,6 +1,9 @@
 """Each pin bites: copies of the oracle with one planted mistake (a dropped
 term, a wrong index, swapped halves, a transposed layout, a wrong rounding
-point) must fail the pins named for it. Runs on the CPU only."""
+point) must fail the pins named for it. Mistakes are planted in oracle.c and
+in the oracle's Python side (oracle/__init__.py: the tolerance bound and the
+marshalling of the sampled k = 8 form). Runs on the CPU only."""
+import importlib.util
 import os
 
 import pytest
@@ -106,6 +109,65 @@ MUTATIONS = {
         "  for (int64_t s = 0; s + 1 < S; ++s) {\n    const int64_t lo",
         ["pin_splitk_exact_and_degenerate", "pin_splitk_normal_and_layouts"]),
 }
+
+
+# Planted in oracle/__init__.py; each copy is loaded as a module of its own
+# and drives the unmodified liboracle.so.
+PY_MUTATIONS = {
+    "abs_mask_keeps_low_half_sign": (
+        "& np.uint32(0x7FFF7FFF)", "& np.uint32(0x7FFFFFFF)", ["pin_bound"]),
+    "abs_mask_keeps_high_half_sign": (
+        "& np.uint32(0x7FFF7FFF)", "& np.uint32(0xFFFF7FFF)", ["pin_bound"]),
+    "bound_c_tensor_not_absolute": (
+        "Ca = None if C is None else np.abs(C)", "Ca = C", ["pin_bound"]),
+    "bound_scalar_c_not_absolute": (
+        "return self.mma(Aa, Ba, Ca, abs(float(c)), dtype)\n"
+        "        return self.mma_sampled(Aa, Ba, Ca, abs(float(c)), dtype, idx)",
+        "return self.mma(Aa, Ba, Ca, float(c), dtype)\n"
+        "        return self.mma_sampled(Aa, Ba, Ca, float(c), dtype, idx)",
+        ["pin_bound"]),
+    "bound_sampled_ignores_c": (
+        "return self.mma_sampled(Aa, Ba, Ca, abs(float(c)), dtype, idx)",
+        "return self.mma_sampled(Aa, Ba, None, abs(float(c)), dtype, idx)",
+        ["pin_bound"]),
+    "k8_sampled_read_as_k16_layout": (
+        "_ptr(C), float(c), batch, M_rep, N_rep, K_rep, 8,",
+        "_ptr(C), float(c), batch, M_rep, N_rep, K_rep // 2, 16,",
+        ["pin_k8_sampled_matches_full"]),
+    "k8_sampled_c_dropped": (
+        "_ptr(C), float(c), batch, M_rep, N_rep, K_rep, 8,",
+        "None, float(c), batch, M_rep, N_rep, K_rep, 8,",
+        ["pin_k8_sampled_matches_full"]),
+}
+
+
+def _run_pins(o, expected):
+    failed = []
+    for pin in expected:
+        try:
+            pins.ALL_PINS[pin](o)
+        except (AssertionError, ValueError):
+            failed.append(pin)
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTATIONS))
+def test_python_side_mutation_is_caught(name, tmp_path):
+    old, new, expected = PY_MUTATIONS[name]
+    path = os.path.join(os.path.dirname(os.path.abspath(oracle.__file__)), "__init__.py")
+    src = open(path).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
+    mod_path = os.path.join(tmp_path, "mutated_oracle.py")
+    with open(mod_path, "w") as f:
+        f.write(src.replace(old, new))
+    spec = importlib.util.spec_from_file_location(f"mutated_oracle_{name}", mod_path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    o = mod.Oracle(oracle.build(force=False))
+    failed = _run_pins(o, expected)
+    assert failed == expected, f"{name}: only {failed} of {expected} caught it"
+    # the unmutated pins pass on the same library
+    assert _run_pins(oracle.default(), expected) == []
 
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
