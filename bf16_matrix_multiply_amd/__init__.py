@@ -24,7 +24,8 @@ import os
 import torch
 
 __all__ = ["BmmError", "pack_operand", "pack_operand_kmajor", "box_copy", "box_store",
-           "box_reduce_add", "mma_tile", "mma_tile_splitk", "splitk_default",
+           "box_reduce_add", "mma_tile", "mma_tile_splitk", "mma_tile_splitk_noalloc",
+           "splitk_default", "NOALLOC_SCRATCH_BYTES",
            "splitk_workspace_bytes", "select_kernel", "library_path", "KERNELS", "MmaOpts",
            "ELEM_TYPES"]
 
@@ -35,6 +36,7 @@ BMM_F16, BMM_BF16 = 0, 1
 _DTYPES = {"f16": BMM_F16, "float16": BMM_F16, torch.float16: BMM_F16,
            "bf16": BMM_BF16, "bfloat16": BMM_BF16, torch.bfloat16: BMM_BF16}
 KERNELS = {"auto": 0, "direct": 1, "tiled": 2, "skinny": 3, "tiled128": 4, "tiled256x128": 5}
+NOALLOC_SCRATCH_BYTES = 64 << 20   # BMM_NOALLOC_SCRATCH_BYTES
 ELEM_TYPES = {"f32": 1, "f16": 2, "bf16": 3, "i32": 4, "i64": 5}
 KERNEL_NAMES = {v: k for k, v in KERNELS.items()}
 
@@ -108,6 +110,8 @@ def lib():
                                          ctypes.POINTER(i64), p]
         L.bmm_mma_tile_splitk.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64, i64,
                                           ctypes.c_int, i32, i32, p, i64, p]
+        L.bmm_mma_tile_splitk_noalloc.argtypes = [p, p, p, p, ctypes.c_float, i64, i64, i64,
+                                                  i64, ctypes.c_int, i32, i32, p]
         L.bmm_mma_splitk_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
         L.bmm_mma_splitk_workspace_bytes.restype = i64
         L.bmm_splitk_default.argtypes = [i64, i64, i64, i64, i32]
@@ -115,7 +119,8 @@ def lib():
                   L.bmm_pack_operand_kmajor_k8,
                   L.bmm_box_copy, L.bmm_mma_tile, L.bmm_mma_tile_with, L.bmm_mma_tile_scaled,
                   L.bmm_mma_tile_opts, L.bmm_select_kernel, L.bmm_box_store,
-                  L.bmm_box_reduce_add, L.bmm_mma_tile_splitk, L.bmm_splitk_default):
+                  L.bmm_box_reduce_add, L.bmm_mma_tile_splitk, L.bmm_mma_tile_splitk_noalloc,
+                  L.bmm_splitk_default):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -330,6 +335,43 @@ def mma_tile_splitk(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = N
     _check(lib().bmm_mma_tile_splitk(_ptr(out), _ptr(A), _ptr(B), _ptr(C), float(c), batch, M_rep,
                                      N_rep, K_rep, dt, atom_k, splits,
                                      _ptr(workspace), ws_bytes, _stream(A)))
+    return out
+
+
+def mma_tile_splitk_noalloc(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None,
+                            c: float = 0.0, dtype=None, splits: int | None = None,
+                            out: torch.Tensor | None = None) -> torch.Tensor:
+    """bmm_mma_tile_splitk_noalloc: the split-K form with its partial sums in
+    the library's static per-device scratch (NOALLOC_SCRATCH_BYTES) instead of
+    a workspace. ``out`` must be given: this call allocates nothing. Calls
+    that overlap on one device race on the scratch."""
+    dt = _dtype_code(dtype, "mma_tile_splitk_noalloc")
+    if out is None:
+        raise ValueError("mma_tile_splitk_noalloc: out is required (this form allocates nothing)")
+    _require_cuda(A, B, C, out)
+    if A.dim() != 5 or B.dim() != 5 or A.shape[3] != 16 or B.shape[3] != 8 or \
+            A.shape[4] not in (8, 4) or B.shape[4] != A.shape[4]:
+        raise ValueError("mma_tile_splitk_noalloc: A must be (batch, M_rep, K_rep, 16, w) and B "
+                         "(batch, N_rep, K_rep, 8, w) packed words, w = 8 or 4")
+    atom_k = 2 * A.shape[4]
+    batch, M_rep, K_rep = A.shape[:3]
+    N_rep = B.shape[1]
+    if B.shape[0] != batch or B.shape[2] != K_rep:
+        raise ValueError("mma_tile_splitk_noalloc: A and B disagree on batch or K_rep")
+    for t, name in ((A, "A"), (B, "B")):
+        if not t.is_contiguous() or t.element_size() != 4:
+            raise ValueError(f"mma_tile_splitk_noalloc: {name} must be a contiguous 32-bit tensor")
+    shape = (batch, M_rep, N_rep, 16, 8)
+    for t, name in ((C, "C"), (out, "out")):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32
+                              or not t.is_contiguous()):
+            raise ValueError(f"mma_tile_splitk_noalloc: {name} must be a contiguous float32 "
+                             f"tensor of shape {shape}")
+    if splits is None:
+        splits = splitk_default(batch, M_rep, N_rep, K_rep, atom_k)
+    _check(lib().bmm_mma_tile_splitk_noalloc(_ptr(out), _ptr(A), _ptr(B), _ptr(C), float(c),
+                                             batch, M_rep, N_rep, K_rep, dt, atom_k, splits,
+                                             _stream(A)))
     return out
 
 

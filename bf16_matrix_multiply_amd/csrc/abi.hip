@@ -99,6 +99,10 @@ int box_store_common(void* dst, const void* img, const bmm_box_desc& d, int elem
 
 }  // namespace
 
+namespace bmm {
+void set_last_error(const std::string& msg) { g_last_error = msg; }
+}  // namespace bmm
+
 extern "C" {
 
 int bmm_abi_version(void) { return 1; }

@@ -18,8 +18,9 @@
  *     choice or transpose).
  *   - Return value: BMM_OK (0) or a negative status; bmm_last_error()
  *     returns a message for the last failure on the calling thread.
- *   - The library allocates no device memory and keeps no device state;
- *     scratch space (the split-K partial sums) is a caller-owned workspace.
+ *   - The library allocates no device memory. Scratch space (the split-K
+ *     partial sums) is a caller-owned workspace, except in
+ *     bmm_mma_tile_splitk_noalloc, which uses a fixed static array per device.
  *   - Destination first (mma.sync page, "Operand coordinates and
  *     ownership": the call takes D, A, B, C).
  */
@@ -351,6 +352,29 @@ int bmm_mma_tile_splitk(float* D, const uint32_t* A, const uint32_t* B, const fl
                         float c_scalar, int64_t batch, int64_t M_rep, int64_t N_rep,
                         int64_t K_rep, bmm_dtype dtype, int32_t atom_k, int32_t splits,
                         float* workspace, int64_t workspace_bytes, void* stream);
+
+/*
+ * bmm_mma_tile_splitk_noalloc — bmm_mma_tile_splitk without a workspace, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. It calls no
+ * allocating routine.
+ *
+ * The partial sums go to a static device array of BMM_NOALLOC_SCRATCH_BYTES
+ * (64 MiB) per device, set up on the first call on that device (the current
+ * device, which must be the device of `stream`) and held until the process
+ * ends. Same arguments, arithmetic, bits and errors as bmm_mma_tile_splitk,
+ * minus the workspace; a request whose partial sums
+ * (bmm_mma_splitk_workspace_bytes) exceed the array returns BMM_ERANGE and
+ * launches nothing. Every call on one device shares that device's array, so
+ * calls that overlap on one device (other streams, other threads) race and
+ * must be serialised by the caller. Nothing in the array needs clearing: each
+ * split writes its whole partial sum before the reduce reads it.
+ */
+#define BMM_NOALLOC_SCRATCH_BYTES (64LL << 20)
+int bmm_mma_tile_splitk_noalloc(float* D, const uint32_t* A, const uint32_t* B, const float* C,
+                                float c_scalar, int64_t batch, int64_t M_rep, int64_t N_rep,
+                                int64_t K_rep, bmm_dtype dtype, int32_t atom_k, int32_t splits,
+                                void* stream);
 
 /* Workspace bytes bmm_mma_tile_splitk needs (0 when K = 0), or < 0. */
 int64_t bmm_mma_splitk_workspace_bytes(int64_t batch, int64_t M_rep, int64_t N_rep,

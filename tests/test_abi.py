@@ -396,3 +396,29 @@ def test_binding_requires_dtype(fn):
         f(A, B, None, 0.0)
     with pytest.raises(ValueError, match="unknown dtype"):
         f(A, B, None, 0.0, "fp8")
+
+
+def test_noalloc_refuses_beyond_its_scratch(L):
+    """The no-allocation split-K form refuses, before any HIP call, a request
+    whose partial sums exceed its static scratch (BMM_ERANGE, a message with
+    the sizes), and passes invalid fields to the regular validation."""
+    assert bmm.NOALLOC_SCRATCH_BYTES == 64 << 20
+    # 1024 x 1024 outputs (4 MiB of D) in 32 splits of 256 steps: 128 MiB of partials
+    rc = L.bmm_mma_tile_splitk_noalloc(P0, P1, P2, None, 0.0, 1, 64, 128, 512, 1, 16, 32, None)
+    assert rc == ERANGE
+    assert "static scratch holds 67108864" in err(L) and "134217728" in err(L)
+    # splits out of range: the regular message, no launch
+    rc = L.bmm_mma_tile_splitk_noalloc(P0, P1, P2, None, 0.0, 1, 64, 128, 512, 1, 16, 0, None)
+    assert rc == EINVAL and "splits" in err(L)
+    rc = L.bmm_mma_tile_splitk_noalloc(P0, P1, P2, None, 0.0, 1, 64, 128, 512, 1, 12, 4, None)
+    assert rc == EINVAL
+
+
+def test_noalloc_binding_requires_out_and_dtype():
+    import torch
+    A = torch.zeros((1, 1, 2, 16, 8), dtype=torch.int32)
+    B = torch.zeros((1, 1, 2, 8, 8), dtype=torch.int32)
+    with pytest.raises(ValueError, match="dtype is required"):
+        bmm.mma_tile_splitk_noalloc(A, B, out=torch.zeros((1, 1, 1, 16, 8)))
+    with pytest.raises(ValueError, match="out is required"):
+        bmm.mma_tile_splitk_noalloc(A, B, None, 0.0, "bf16")
