@@ -4,14 +4,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <string>
-
 #include "../../include/bmm.h"
 
 namespace bmm {
-
-// Sets the message bmm_last_error returns on this thread.
-void set_last_error(const std::string& msg);
 
 struct MmaArgs {
   float* D;

@@ -15,6 +15,10 @@ struct Status {
   bool ok() const { return code == BMM_OK; }
 };
 
+// Sets the message bmm_last_error returns on this thread (defined with the
+// entry points).
+void set_last_error(const std::string& msg);
+
 Status check_pack(const uint32_t* dst, const uint16_t* src, int64_t batch, int64_t rows,
                   int64_t K, int64_t ld_src, int32_t atom_rows, int32_t atom_k);
 
