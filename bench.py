@@ -13,7 +13,10 @@ as a whole. ``roofline`` is for the step's dominant kernel, timed with HIP
 events on the stream it runs on in a second pass of K steps (an event after
 each kernel: the events cost GPU time, so they stay out of the first pass);
 ``cpu_baseline`` is the CPU oracle timed on a bounded sample of the same
-workload on this host's cores.
+workload on this host's cores. The default (headline) run also adds
+``extra_records``: the multiply alone on the 4096^3 f16 configuration against
+the MFMA peak, and on the skinny 16 x 16384 x 16384 one against HBM (warm and
+after a cache flush), each with its own traffic record.
 
     python bench.py --op box_copy|box_store|box_reduce_add
 
@@ -244,6 +247,75 @@ def run_box(args, torch, bmm):
     print(json.dumps(line), flush=True)
 
 
+# The other two configurations with a roofline target, measured in the same
+# run as extra records of the default (headline) line: 4096^3 f16 against the
+# MFMA peak, and the skinny M = 16 shape against HBM (warm, and after a cache
+# flush). Each times the multiply alone with an event pair around every call.
+EXTRA_RECORDS = ("gemm_4096_f16_quarter", "skinny_16x16384x16384_bf16")
+
+
+def multiply_record(name, torch, bmm, steps):
+    w = workloads.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    inp = workloads.make_inputs(w, seed=0)
+    a = torch.from_numpy(inp["a"].view(np.int16)).to(dev)
+    b = torch.from_numpy(inp["b"].view(np.int16)).to(dev)
+    A, B = bmm.pack_operand(a, 16), bmm.pack_operand(b, 8)
+    del a, b
+    C = None if inp["c_tensor"] is None else torch.from_numpy(inp["c_tensor"]).to(dev)
+    c = float(inp["c_scalar"])
+    D = torch.empty((w.batch, w.M_rep, w.N_rep, 16, 8), dtype=torch.float32, device=dev)
+    kernel = bmm.select_kernel(w.batch, w.M_rep, w.N_rep, w.K_rep)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        bmm.mma_tile(A, B, C, c, w.dtype, out=D)
+
+    warm_up(call, 5, torch)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for e in evs:
+        e[0].record(stream)
+        call()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    hbm = w.flops / w.algorithmic_bytes < RIDGE_FLOP_PER_BYTE
+    rec = {"workload": w.name, "kernel": f"mma_tile[{kernel}]", "dtype": w.dtype,
+           "M": w.M, "N": w.N, "K": w.K, "c": "tensor" if w.c_tensor else "scalar",
+           "avg_launch_us": round(us, 2), "tflops": round(w.flops / us / 1e6, 2),
+           "gbs": round(w.algorithmic_bytes / us / 1e3, 1),
+           "algorithmic_bytes_per_launch": w.algorithmic_bytes,
+           "traffic": traffic_from_profiles("mma_tile", w.name, "", kernel)}
+    if hbm:
+        rec.update({"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "achieved": rec["gbs"], "frac": round(rec["gbs"] / PEAK_HBM_GBS, 4)})
+        flush = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+        cold = []
+        for _ in range(10):
+            flush.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            cold.append((e0, e1))
+        torch.cuda.synchronize()
+        cold_us = float(np.mean([x.elapsed_time(y) * 1e3 for x, y in cold]))
+        del flush
+        rec.update({"cold_us": round(cold_us, 2),
+                    "cold_achieved": round(w.algorithmic_bytes / cold_us / 1e3, 1),
+                    "cold_frac": round(w.algorithmic_bytes / cold_us / 1e3 / PEAK_HBM_GBS, 4)})
+    else:
+        rec.update({"bound": "mfma", "peak": PEAK_MFMA_TFLOPS[w.dtype], "unit": "TFLOP/s",
+                    "achieved": rec["tflops"],
+                    "frac": round(rec["tflops"] / PEAK_MFMA_TFLOPS[w.dtype], 4)})
+    log(f"[bench] extra record {w.name}: mma_tile[{kernel}] {us:.1f} us, "
+        f"{rec['achieved']} {rec['unit']} ({rec['frac']:.3f} of peak)"
+        + (f"; after a cache flush {rec['cold_us']} us ({rec['cold_frac']:.3f})" if hbm else ""))
+    del A, B, C, D
+    torch.cuda.empty_cache()
+    return rec
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,6 +345,9 @@ def main():
     ap.add_argument("--context", action="store_true",
                     help="also time torch.matmul (the vendor library) on the same logical operands, "
                          "for context only")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the extra records of the 4096^3 and skinny configurations that "
+                         "the default (headline) run adds")
     ap.add_argument("--splitk", type=int, default=None,
                     help="run the split-K form with this many splits (0: the library's default)")
     args = ap.parse_args()
@@ -485,6 +560,11 @@ def main():
     }
     if context is not None:
         line["context"] = context
+    default_run = (w.name == workloads.HEADLINE and args.kernel == "auto" and not args.kmajor
+                   and ka == 16 and splits is None and args.alpha is None and args.beta is None)
+    if default_run and not args.no_extra:
+        line["extra_records"] = {n: multiply_record(n, torch, bmm, args.steps)
+                                 for n in EXTRA_RECORDS}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a sample of the same workload")
         line["cpu_baseline"] = cpu_baseline(w, inp, D.cpu().numpy(), args.cpu_seconds, args.alpha,

@@ -51,12 +51,57 @@ def assert_parity_full(w, inp, D, kernel=""):
         assert (err <= BOUND_SCALE * bnd).all(), f"{w.name}/{kernel}: worst err/bound {ratio}"
 
 
-def assert_parity_sampled(w, inp, D, count=2048, seed=11, A=None, B=None):
-    """Sampled outputs (random + corners) against the oracle computed one by one."""
+def per_tile_indices(w, tile_m=256, tile_n=256, per_tile=2, seed=13):
+    """(count, 3) samples with ``per_tile`` random outputs inside every
+    tile_m x tile_n block of D (every macro tile, so every workgroup slot and
+    every XCD of the launch), plus the last row and column."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for b in range(w.batch):
+        for m0 in range(0, w.M, tile_m):
+            hm = min(tile_m, w.M - m0)
+            for n0 in range(0, w.N, tile_n):
+                hn = min(tile_n, w.N - n0)
+                for _ in range(per_tile):
+                    out.append((b, m0 + rng.integers(0, hm), n0 + rng.integers(0, hn)))
+        out += [(b, w.M - 1, n) for n in (0, w.N - 1)] + [(b, m, w.N - 1) for m in (0, w.M // 2)]
+    return np.array(out, np.int64)
+
+
+def assert_quarter_sums(w, inp, D):
+    """Quarter-integer operands (and C on the quarter grid): every product and
+    partial sum is exact in fp32, so 16*D is an integer matrix whose every row
+    sum and column sum equals its int64 closed form
+    16*C + sum_k (4a)(4b) (mma.sync page, worked 16x8 example: the result is
+    a.b^T exactly). Checks every output of D through its row and column."""
+    assert w.exact
+    Dl = util.tile_to_logical(D).astype(np.float64)
+    assert not np.isnan(Dl).any(), f"{w.name}: unwritten (NaN-poisoned) outputs"
+    D16 = np.rint(Dl * 16).astype(np.int64)
+    assert np.array_equal(D16.astype(np.float64), Dl * 16), f"{w.name}: off the 1/16 grid"
+    if inp["c_tensor"] is not None:
+        C16 = np.rint(util.tile_to_logical(inp["c_tensor"]).astype(np.float64) * 16).astype(np.int64)
+    else:
+        C16 = np.full(D16.shape, int(round(16 * float(inp["c_scalar"]))), np.int64)
+    for b in range(w.batch):
+        ai = np.rint(4 * util.decode(inp["a"][b], w.dtype)).astype(np.int64)
+        bi = np.rint(4 * util.decode(inp["b"][b], w.dtype)).astype(np.int64)
+        rows = C16[b].sum(axis=1) + ai @ bi.sum(axis=0)
+        cols = C16[b].sum(axis=0) + bi @ ai.sum(axis=0)
+        bad_r = np.nonzero(D16[b].sum(axis=1) != rows)[0]
+        bad_c = np.nonzero(D16[b].sum(axis=0) != cols)[0]
+        assert bad_r.size == 0 and bad_c.size == 0, \
+            f"{w.name}: rows {bad_r[:4].tolist()} and columns {bad_c[:4].tolist()} differ"
+
+
+def assert_parity_sampled(w, inp, D, count=2048, seed=11, A=None, B=None, idx=None):
+    """Sampled outputs (random + corners, or the given ``idx``) against the
+    oracle computed one by one."""
     if A is None:
         A, B = oracle_operands(w, inp)
     rng = np.random.default_rng(seed)
-    idx = util.sample_indices(rng, w.batch, w.M, w.N, count)
+    if idx is None:
+        idx = util.sample_indices(rng, w.batch, w.M, w.N, count)
     ref = oracle.mma_sampled(A, B, inp["c_tensor"], inp["c_scalar"], w.dtype, idx)
     Dl = util.tile_to_logical(D)
     got = Dl[idx[:, 0], idx[:, 1], idx[:, 2]]

@@ -179,17 +179,21 @@ def test_full_gemm_4096_f16_quarter():
 
 
 def test_full_skinny_bf16():
+    """16 x 16384 x 16384: outputs sampled in every 16 x 64 column block of the
+    skinny kernel (one workgroup's share), within bound."""
     w = workloads.WORKLOADS["skinny_16x16384x16384_bf16"]
     inp = inputs(w)
     _, _, _, D = gu.gpu_run(w, inp)
-    gu.assert_parity_sampled(w, inp, D, count=4096)
+    gu.assert_parity_sampled(w, inp, D, idx=gu.per_tile_indices(w, 16, 64, per_tile=2))
 
 
 def test_full_gemm_8192_bf16_ctensor():
+    """8192^3 with the C tensor: two outputs sampled in every 256 x 256 macro
+    tile (all 1024 tiles, so every workgroup slot on every XCD), within bound."""
     w = workloads.WORKLOADS["gemm_8192_bf16_ctensor"]
     inp = inputs(w)
     _, _, _, D = gu.gpu_run(w, inp)
-    gu.assert_parity_sampled(w, inp, D)
+    gu.assert_parity_sampled(w, inp, D, idx=gu.per_tile_indices(w, 256, 256, per_tile=2))
 
 
 @pytest.mark.parametrize("name", ["shard_n8_8192x1024x8192_bf16_ctensor",
@@ -202,19 +206,37 @@ def test_full_shard_256x128_sampled(name):
     assert bmm.select_kernel(w.batch, w.M_rep, w.N_rep, w.K_rep) == "tiled256x128"
     inp = workloads.make_inputs(w, seed=0)
     _, _, _, D = gu.gpu_run(w, inp)
-    gu.assert_parity_sampled(w, inp, D)
+    gu.assert_parity_sampled(w, inp, D, idx=gu.per_tile_indices(w, 256, 128, per_tile=2))
+
+
+@pytest.mark.parametrize("name", ["shard_n8_8192x1024x8192_bf16_ctensor",
+                                  "shard_m8_1024x8192x8192_bf16_ctensor"])
+def test_full_shard_256x128_quarter_sums(name):
+    """The shard shapes on the 256 x 128 tile with quarter-integer operands and
+    C on the quarter grid: every row and column sum of 16*D equals its int64
+    closed form, so every output is checked."""
+    base = workloads.EXTRA_WORKLOADS[name]
+    w = C(1, base.M, base.N, base.K, "bf16", "quarter", "quarter", c_tensor=True,
+          name=name + "_quarter")
+    inp = workloads.make_inputs(w, seed=4)
+    _, _, _, D = gu.gpu_run(w, inp, "tiled256x128")
+    gu.assert_quarter_sums(w, inp, D)
 
 
 @pytest.mark.parametrize("name", ["skinny_16x16384x16384_bf16", "gemm_8192_bf16_ctensor"])
 def test_full_quantised_variants(name):
-    """The large bf16 shapes with quarter-integer operands: bit-exact samples
-    (|D| <= K with a 1/16 grid needs at most 19 bits)."""
+    """The large bf16 shapes with quarter-integer operands and C on the
+    quarter grid (|D| <= 16 + K on a 1/16 grid: at most 19 bits, exact): every
+    row and column sum of 16*D equals its int64 closed form, and samples in
+    every macro tile are bit-exact against the oracle."""
     base = workloads.WORKLOADS[name]
     w = C(base.batch, base.M, base.N, base.K, "bf16", "quarter", "quarter",
-          c_tensor=False, name=name + "_quarter")
+          c_tensor=True, name=name + "_quarter")
     inp = workloads.make_inputs(w, seed=1)
     _, _, _, D = gu.gpu_run(w, inp)
-    gu.assert_parity_sampled(w, inp, D)
+    gu.assert_quarter_sums(w, inp, D)
+    tm, tn = (256, 256) if w.M >= 256 else (16, 64)
+    gu.assert_parity_sampled(w, inp, D, idx=gu.per_tile_indices(w, tm, tn, per_tile=1))
 
 
 @pytest.mark.parametrize("shape,kernel", [((2048, 2048, 2048), "auto"),
