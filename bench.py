@@ -254,6 +254,52 @@ def run_box(args, torch, bmm):
 EXTRA_RECORDS = ("gemm_4096_f16_quarter", "skinny_16x16384x16384_bf16")
 
 
+def power_sample(call, torch, seconds=3.0, settle=1.0):
+    """Socket power and per-XCD gfx clocks (amd-smi) while ``call`` runs back
+    to back for ``seconds``; samples from the first ``settle`` seconds are
+    dropped (the telemetry lags by about half a second). None without amd-smi."""
+    import re
+    import shutil
+    import subprocess
+    import threading
+    if shutil.which("amd-smi") is None:
+        return None
+    samples, stop = [], [False]
+    t0 = time.perf_counter()
+
+    def sampler():
+        while not stop[0]:
+            r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True,
+                               text=True)
+            pw = re.search(r'"socket_power":\s*\{\s*"value":\s*(\d+)', r.stdout)
+            ck = [int(x) for x in re.findall(
+                r'"gfx_\d+":\s*\{\s*"clk":\s*\{\s*"value":\s*(\d+)', r.stdout)]
+            if pw:
+                samples.append((time.perf_counter() - t0, int(pw.group(1)), ck))
+
+    th = threading.Thread(target=sampler)
+    th.start()
+    calls = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            call()
+        torch.cuda.synchronize()
+        calls += 10
+    elapsed = time.perf_counter() - t0
+    stop[0] = True
+    th.join()
+    settled = [x for x in samples if x[0] >= settle]
+    if not settled:
+        return None
+    watts = np.array([x[1] for x in settled])
+    clocks = np.array([x[2] for x in settled if x[2]])
+    return {"tool": "amd-smi metric -p -c", "samples": len(settled),
+            "socket_w_median": float(np.median(watts)), "socket_w_max": int(watts.max()),
+            "gfx_clock_mhz_median_per_xcd": [int(v) for v in np.median(clocks, axis=0)]
+            if len(clocks) else None,
+            "us_per_call_wall": round(elapsed / calls * 1e6, 1)}
+
+
 def multiply_record(name, torch, bmm, steps):
     w = workloads.WORKLOADS[name]
     dev = torch.device("cuda:0")
@@ -345,6 +391,9 @@ def main():
     ap.add_argument("--context", action="store_true",
                     help="also time torch.matmul (the vendor library) on the same logical operands, "
                          "for context only")
+    ap.add_argument("--power", action="store_true",
+                    help="also sample socket power and gfx clocks (amd-smi) while the multiply "
+                         "runs back to back for 3 s")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra records of the 4096^3 and skinny configurations that "
                          "the default (headline) run adds")
@@ -560,6 +609,9 @@ def main():
     }
     if context is not None:
         line["context"] = context
+    if args.power:
+        line["power"] = power_sample(multiply, torch)
+        log(f"[bench] power while the multiply runs: {line['power']}")
     default_run = (w.name == workloads.HEADLINE and args.kernel == "auto" and not args.kmajor
                    and ka == 16 and splits is None and args.alpha is None and args.beta is None)
     if default_run and not args.no_extra:
