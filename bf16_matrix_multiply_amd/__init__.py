@@ -25,7 +25,7 @@ import torch
 
 __all__ = ["BmmError", "pack_operand", "pack_operand_kmajor", "box_copy", "box_store",
            "box_reduce_add", "mma_tile", "mma_tile_splitk", "mma_tile_splitk_noalloc",
-           "splitk_default", "NOALLOC_SCRATCH_BYTES",
+           "splitk_default", "splitk_suggested", "NOALLOC_SCRATCH_BYTES",
            "splitk_workspace_bytes", "select_kernel", "library_path", "KERNELS", "MmaOpts",
            "ELEM_TYPES"]
 
@@ -115,12 +115,13 @@ def lib():
         L.bmm_mma_splitk_workspace_bytes.argtypes = [i64, i64, i64, i64, i32, i32]
         L.bmm_mma_splitk_workspace_bytes.restype = i64
         L.bmm_splitk_default.argtypes = [i64, i64, i64, i64, i32]
+        L.bmm_splitk_suggested.argtypes = [i64, i64, i64, i64, i32]
         for f in (L.bmm_pack_operand, L.bmm_pack_operand_kmajor, L.bmm_pack_operand_k8,
                   L.bmm_pack_operand_kmajor_k8,
                   L.bmm_box_copy, L.bmm_mma_tile, L.bmm_mma_tile_with, L.bmm_mma_tile_scaled,
                   L.bmm_mma_tile_opts, L.bmm_select_kernel, L.bmm_box_store,
                   L.bmm_box_reduce_add, L.bmm_mma_tile_splitk, L.bmm_mma_tile_splitk_noalloc,
-                  L.bmm_splitk_default):
+                  L.bmm_splitk_default, L.bmm_splitk_suggested):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -291,6 +292,12 @@ def splitk_workspace_bytes(batch, M_rep, N_rep, K_rep, atom_k, splits) -> int:
 
 def splitk_default(batch, M_rep, N_rep, K_rep, atom_k=16) -> int:
     return _check(lib().bmm_splitk_default(batch, M_rep, N_rep, K_rep, atom_k))
+
+
+def splitk_suggested(batch, M_rep, N_rep, K_rep, atom_k=16) -> int:
+    """bmm_splitk_suggested: the split count when mma_tile_splitk is expected
+    to beat mma_tile for this shape, else 1."""
+    return _check(lib().bmm_splitk_suggested(batch, M_rep, N_rep, K_rep, atom_k))
 
 
 def mma_tile_splitk(A: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None = None,

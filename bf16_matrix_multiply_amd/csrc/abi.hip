@@ -320,6 +320,26 @@ int bmm_splitk_default(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_re
   return int(s < 1 ? 1 : s);
 }
 
+// Whether the split-K form beats the plain entry point for a shape, from the
+// sweep of both over 33 shapes (bf16, normal operands; MI355X). Splitting won
+// exactly where K >= 4096, M >= 32, AUTO would run the skinny or the 128 x 128
+// kernel and the default split count is above one: 1024 x 1024 x 8192 (30.0
+// against 39.7 us), 2048 x 1024 x 4096 (29.1 / 34.0), 256 x 4096 x 4096
+// (22.0 / 24.0), 64 x 8192 x 8192 (27.4 / 43.7), 32 x 16384 x 4096 (26.3 /
+// 28.8), 1024 x 1024 x 65536 (123.3 / 335.1). It lost with K = 2048
+// (512 x 2048 x 2048: 20.2 / 13.1), with M = 16 (16 x 16384 x 16384, where the
+// skinny kernel streams B once: 106.8 / 85.7) and on the 256 x 128 tile
+// (8192 x 1024 x 8192: 121.4 / 112.3).
+int bmm_splitk_suggested(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep,
+                         int32_t atom_k) {
+  const int s = bmm_splitk_default(batch, M_rep, N_rep, K_rep, atom_k);
+  if (s <= 1) return s;
+  const int64_t K = K_rep * atom_k;
+  const int k = choose_kernel(batch, M_rep, N_rep, K);
+  return K >= 4096 && M_rep >= 2 && (k == BMM_KERNEL_SKINNY || k == BMM_KERNEL_TILED_128) ? s
+                                                                                        : 1;
+}
+
 int bmm_mma_tile_splitk(float* D, const uint32_t* A, const uint32_t* B, const float* C,
                         float c_scalar, int64_t batch, int64_t M_rep, int64_t N_rep,
                         int64_t K_rep, bmm_dtype dtype, int32_t atom_k, int32_t splits,

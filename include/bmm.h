@@ -262,6 +262,9 @@ int bmm_box_reduce_add(void* dst, const void* src_image, const bmm_box_desc* des
  * N_rep is a no-op; K_rep = 0 gives D = C (the empty sum).
  * Summation order inside the hardware's 32-deep MFMA step is the hardware's;
  * between steps K is taken in ascending order from C.
+ * This entry point takes no workspace and so never splits K: for shapes with
+ * few output tiles and a long K, bmm_splitk_suggested says when
+ * bmm_mma_tile_splitk is faster, and with how many splits.
  * Errors: BMM_EINVAL, BMM_EALIGN, BMM_EOVERLAP, BMM_EHIP.
  */
 int bmm_mma_tile(float* D, const uint32_t* A, const uint32_t* B, const float* C,
@@ -387,6 +390,15 @@ int64_t bmm_mma_splitk_workspace_bytes(int64_t batch, int64_t M_rep, int64_t N_r
  * and 128 x 128 tiles otherwise.) */
 int bmm_splitk_default(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep,
                        int32_t atom_k);
+
+/* Whether to call bmm_mma_tile_splitk instead of bmm_mma_tile for this
+ * shape: the split count to use when the split-K form is expected to be the
+ * faster of the two (shapes with few output tiles and a long K, e.g.
+ * 1024 x 1024 x 65536: 123 against 335 us on MI355X), 1 when the plain entry
+ * point is expected to be at least as fast, or < 0 for invalid extents. The
+ * plain entry point never splits K itself, since it takes no workspace. */
+int bmm_splitk_suggested(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep,
+                         int32_t atom_k);
 
 /* Which kernel AUTO would run for this shape (K_rep in 16-deep atoms; a
  * bmm_kernel value), or < 0. */

@@ -422,3 +422,39 @@ def test_noalloc_binding_requires_out_and_dtype():
         bmm.mma_tile_splitk_noalloc(A, B, out=torch.zeros((1, 1, 1, 16, 8)))
     with pytest.raises(ValueError, match="out is required"):
         bmm.mma_tile_splitk_noalloc(A, B, None, 0.0, "bf16")
+
+
+# (M, N, K, default split-K us, plain entry point us): the sweep of both forms on
+# MI355X (bf16 normal operands, no C; profiles/kernel_choice_sweep.md).
+SWEEP = [(128, 128, 256, 16.9, 12.8), (512, 512, 512, 17.2, 13.5), (1024, 1024, 1024, 17.5, 13.5),
+         (1536, 1536, 1536, 22.7, 18.2), (2048, 2048, 2048, 30.6, 24.2),
+         (2560, 2560, 2560, 47.0, 35.9), (3072, 3072, 3072, 70.8, 59.6),
+         (4096, 4096, 1024, 57.8, 38.4), (4096, 4096, 4096, 124.5, 103.9),
+         (8192, 8192, 8192, 844.6, 777.7), (1024, 1024, 8192, 30.0, 39.7),
+         (2048, 2048, 8192, 77.1, 71.0), (1024, 4096, 4096, 45.7, 39.2),
+         (2048, 1024, 4096, 29.1, 34.0), (1024, 1024, 65536, 123.3, 335.1),
+         (512, 512, 65536, 48.6, 272.4), (16, 1024, 1024, 14.7, 12.7), (64, 2048, 2048, 15.3, 13.6),
+         (256, 4096, 4096, 22.0, 24.0), (512, 2048, 2048, 20.2, 13.1), (64, 8192, 8192, 27.4, 43.7),
+         (32, 16384, 4096, 26.3, 28.8), (16, 16384, 16384, 106.8, 85.7),
+         (8192, 1024, 8192, 121.4, 112.3), (1024, 8192, 8192, 121.8, 112.5),
+         (2304, 2304, 4096, 59.9, 47.4), (3072, 2048, 4096, 64.1, 51.1),
+         (2816, 2816, 4096, 73.6, 59.6), (2304, 2048, 4096, 61.6, 51.0),
+         (2048, 2304, 4096, 59.9, 47.8), (2560, 2048, 4096, 61.8, 48.5),
+         (2304, 2304, 2304, 41.6, 31.2), (2048, 2560, 8192, 109.0, 87.5)]
+
+
+@pytest.mark.parametrize("M,N,K,split_us,plain_us", SWEEP)
+def test_splitk_suggested_matches_the_sweep(L, M, N, K, split_us, plain_us):
+    """bmm_splitk_suggested says to split exactly where the measured default
+    split-K form beat the plain entry point, and then gives that split count."""
+    s = L.bmm_splitk_suggested(1, M // 16, N // 8, K // 16, 16)
+    assert (s > 1) == (split_us < plain_us), (M, N, K, s)
+    if s > 1:
+        assert s == L.bmm_splitk_default(1, M // 16, N // 8, K // 16, 16)
+    assert bmm.splitk_suggested(1, M // 16, N // 8, K // 16) == s
+
+
+def test_splitk_suggested_rejects_invalid(L):
+    assert L.bmm_splitk_suggested(-1, 1, 1, 1, 16) == EINVAL
+    assert L.bmm_splitk_suggested(1, 1, 1, 1, 12) == EINVAL
+    assert L.bmm_splitk_suggested(1, 0, 0, 0, 16) == 1
