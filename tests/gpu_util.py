@@ -83,11 +83,28 @@ def assert_quarter_sums(w, inp, D):
         C16 = np.rint(util.tile_to_logical(inp["c_tensor"]).astype(np.float64) * 16).astype(np.int64)
     else:
         C16 = np.full(D16.shape, int(round(16 * float(inp["c_scalar"]))), np.int64)
+    # The operands are multiples of 1/4 with |x| <= 1, so every product and
+    # every partial sum of these row and column totals is a multiple of 1/16
+    # far below 2^48: float64 (BLAS) computes them exactly.
+    chunk = 1 << 18   # K values decoded at a time (long-K cases hold GBs of operands)
     for b in range(w.batch):
-        ai = np.rint(4 * util.decode(inp["a"][b], w.dtype)).astype(np.int64)
-        bi = np.rint(4 * util.decode(inp["b"][b], w.dtype)).astype(np.int64)
-        rows = C16[b].sum(axis=1) + ai @ bi.sum(axis=0)
-        cols = C16[b].sum(axis=0) + bi @ ai.sum(axis=0)
+        rows = np.zeros(w.M, np.float64)
+        cols = np.zeros(w.N, np.float64)
+        half = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+        for k0 in range(0, w.K, chunk):
+            # decoded on the host by torch's own half -> float64 conversion
+            ai = torch.from_numpy(np.ascontiguousarray(inp["a"][b][:, k0:k0 + chunk])
+                                  .view(np.int16)).view(half).to(torch.float64)
+            bi = torch.from_numpy(np.ascontiguousarray(inp["b"][b][:, k0:k0 + chunk])
+                                  .view(np.int16)).view(half).to(torch.float64)
+            assert float(ai.abs().max()) <= 1 and float(bi.abs().max()) <= 1
+            rows += (ai @ bi.sum(dim=0)).numpy()
+            cols += (bi @ ai.sum(dim=0)).numpy()
+        assert max(np.abs(rows).max(), np.abs(cols).max()) < 2.0 ** 44
+        r16, c16 = rows * 16, cols * 16
+        assert np.array_equal(r16, np.rint(r16)) and np.array_equal(c16, np.rint(c16))
+        rows = C16[b].sum(axis=1) + r16.astype(np.int64)
+        cols = C16[b].sum(axis=0) + c16.astype(np.int64)
         bad_r = np.nonzero(D16[b].sum(axis=1) != rows)[0]
         bad_c = np.nonzero(D16[b].sum(axis=0) != cols)[0]
         assert bad_r.size == 0 and bad_c.size == 0, \

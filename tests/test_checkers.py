@@ -9,9 +9,11 @@ import workloads
 from tests import gpu_util as gu
 
 
+@pytest.mark.parametrize("dtype,dist", [("bf16", "quarter"), ("f16", "quarter"),
+                                        ("bf16", "ternary"), ("f16", "ternary")])
 @pytest.mark.parametrize("c_tensor", [True, False])
-def test_quarter_sums_accept_oracle_and_catch_one_output(c_tensor):
-    w = workloads.custom(2, 48, 40, 96, "bf16", "quarter", "quarter", c_tensor=c_tensor,
+def test_quarter_sums_accept_oracle_and_catch_one_output(c_tensor, dtype, dist):
+    w = workloads.custom(2, 48, 40, 96, dtype, dist, dist, c_tensor=c_tensor,
                          c_scalar=-1.25, name="checker")
     inp = workloads.make_inputs(w, seed=2)
     A, B = oracle.pack(inp["a"], 16), oracle.pack(inp["b"], 8)

@@ -239,6 +239,37 @@ def test_full_quantised_variants(name):
     gu.assert_parity_sampled(w, inp, D, idx=gu.per_tile_indices(w, tm, tn, per_tile=1))
 
 
+def test_largest_k_of_the_tiled_kernels():
+    """The tiled kernels take K < 2^22 values, where one tile's buffer offsets
+    reach 2 GB. At K = 2^22 - 4096 with one full 256 x 256 tile, ternary
+    operands and C on the quarter grid (every partial sum exact), the three
+    tile shapes and the split-K form give the same bits, outputs sampled over
+    the tile equal the oracle's, and every row and column sum of 16*D equals
+    its int64 closed form."""
+    K = (1 << 22) - 4096
+    w = C(1, 256, 256, K, "bf16", "ternary", "ternary", c_tensor=True, name="largest_k")
+    inp = workloads.make_inputs(w, seed=5)
+    print(f"[largest_k] {w.M}x{w.N}x{w.K}", flush=True)
+    a, b = gu.dev_u16(inp["a"]), gu.dev_u16(inp["b"])
+    A, B = bmm.pack_operand(a, 16), bmm.pack_operand(b, 8)
+    del a, b
+    Cd = torch.from_numpy(inp["c_tensor"]).cuda()
+    shape = (1, w.M_rep, w.N_rep, 16, 8)
+    outs = {}
+    for k in ("tiled", "tiled256x128", "tiled128"):
+        out = torch.full(shape, float("nan"), device="cuda")
+        outs[k] = bmm.mma_tile(A, B, Cd, 0.0, "bf16", out=out, kernel=k).cpu().numpy()
+    out = torch.full(shape, float("nan"), device="cuda")
+    outs["splitk4"] = bmm.mma_tile_splitk(A, B, Cd, 0.0, "bf16", 4, out=out).cpu().numpy()
+    del A, B
+    torch.cuda.empty_cache()
+    ref = outs["tiled"]
+    for k, D in outs.items():
+        assert np.array_equal(D.view(np.uint32), ref.view(np.uint32)), k
+    gu.assert_quarter_sums(w, inp, ref)
+    gu.assert_parity_sampled(w, inp, ref, idx=gu.per_tile_indices(w, 32, 32, per_tile=1))
+
+
 @pytest.mark.parametrize("shape,kernel", [((2048, 2048, 2048), "auto"),
                                           ((2560, 1536, 4096), "tiled128"),
                                           ((4096, 4096, 4096), "tiled128")])

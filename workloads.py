@@ -13,6 +13,9 @@ B, C):
   result with two K16 issues"). These values are exact in f16 and bf16.
 * ``normal``: ``standard_normal(float32) * scale``, rounded once to bf16 with
   round-to-nearest-even (or to f16 with numpy's own round-to-nearest-even).
+* ``ternary``: -1/4, 0 or 1/4, uniformly (integers in [0, 2] mapped to those
+  three values), for exact cases with a very long K: every product is 0 or
+  1/16 in magnitude, so partial sums stay exact in fp32 up to K = 2^24.
 * C, when it is a tensor, is standard normal float32 (or, for the exact
   quarter-integer cases, integers in [-64, 64] divided by 4) drawn directly in
   the atom-tiled accumulator layout (batch, M/16, N/8, 16, 8); the draws are
@@ -127,7 +130,16 @@ HEADLINE = "gemm_8192_bf16_ctensor"
 SKINNY = "skinny_16x16384x16384_bf16"
 
 
+# bit patterns of -1/4, 0 and 1/4 in each format (exact in both)
+_TERNARY_BITS = {F16: np.array([0xB400, 0x0000, 0x3400], np.uint16),
+                 BF16: np.array([0xBE80, 0x0000, 0x3E80], np.uint16)}
+
+
 def draw_operand(rng: np.random.Generator, dist: str, shape, dtype: str, scale: float = 1.0):
+    if dist == "ternary":
+        # -1/4, 0 or 1/4 uniformly: every product is 0 or +-1/16, so sums of up
+        # to 2^24 products are exact in fp32 (long-K exact cases)
+        return _TERNARY_BITS[dtype][rng.integers(0, 3, shape, dtype=np.int8)]
     if dist == "quarter":
         vals = rng.integers(-4, 5, shape) / 4
         if dtype == F16:
@@ -163,7 +175,7 @@ def make_inputs(w: Workload, seed: int = 0, a_dist: str | None = None,
 
 def custom(batch, M, N, K, dtype=BF16, a_dist="normal", b_dist="normal", c_tensor=False,
            c_scalar=0.0, b_scale=1.0, name="custom") -> Workload:
-    exact = a_dist == "quarter" and b_dist == "quarter"
+    exact = a_dist in ("quarter", "ternary") and b_dist in ("quarter", "ternary")
     return Workload(name, batch, M, N, K, dtype, a_dist, b_dist, b_scale, c_tensor, c_scalar,
                     exact=exact, c_dist="quarter" if exact else "normal")
 
