@@ -254,11 +254,20 @@ def run_box(args, torch, bmm):
 EXTRA_RECORDS = ("gemm_4096_f16_quarter", "skinny_16x16384x16384_bf16")
 
 
+def parse_amd_smi_metric(text: str):
+    """(socket power in W, [gfx clock in MHz of each XCD]) from the JSON that
+    `amd-smi metric -p -c --json` prints for one GPU; (None, []) if absent."""
+    import re
+    pw = re.search(r'"socket_power":\s*\{\s*"value":\s*(\d+)', text)
+    ck = [int(x) for x in re.findall(r'"gfx_\d+":\s*\{\s*"clk":\s*\{\s*"value":\s*(\d+)',
+                                     text)]
+    return (int(pw.group(1)) if pw else None), ck
+
+
 def power_sample(call, torch, seconds=3.0, settle=1.0):
     """Socket power and per-XCD gfx clocks (amd-smi) while ``call`` runs back
     to back for ``seconds``; samples from the first ``settle`` seconds are
     dropped (the telemetry lags by about half a second). None without amd-smi."""
-    import re
     import shutil
     import subprocess
     import threading
@@ -271,11 +280,9 @@ def power_sample(call, torch, seconds=3.0, settle=1.0):
         while not stop[0]:
             r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True,
                                text=True)
-            pw = re.search(r'"socket_power":\s*\{\s*"value":\s*(\d+)', r.stdout)
-            ck = [int(x) for x in re.findall(
-                r'"gfx_\d+":\s*\{\s*"clk":\s*\{\s*"value":\s*(\d+)', r.stdout)]
-            if pw:
-                samples.append((time.perf_counter() - t0, int(pw.group(1)), ck))
+            watts, clocks = parse_amd_smi_metric(r.stdout)
+            if watts is not None:
+                samples.append((time.perf_counter() - t0, watts, clocks))
 
     th = threading.Thread(target=sampler)
     th.start()

@@ -81,3 +81,57 @@ def test_traffic_records_per_configuration():
     assert bench.traffic_from_profiles("mma_tile", "gemm_8192_bf16_ctensor", "", "tiled") == got
     assert bench.traffic_from_profiles("mma_tile", "gemm_8192_bf16_ctensor", "", "skinny") is None
     assert bench.traffic_from_profiles("pack_operand_kmajor", "gemm_8192_bf16_ctensor") > 0
+
+
+# The shape of `amd-smi metric -p -c --json` for one GPU (two of its eight XCD
+# clocks shown), as the tool printed it on an MI355X machine.
+AMD_SMI_SAMPLE = """{
+    "gpu_data": [
+        {
+            "gpu": 0,
+            "power": {
+                "socket_power": {
+                    "value": 1397,
+                    "unit": "W"
+                },
+                "gfx_voltage": "N/A",
+                "throttle_status": "N/A"
+            },
+            "clock": {
+                "gfx_0": {
+                    "clk": {
+                        "value": 1558,
+                        "unit": "MHz"
+                    },
+                    "min_clk": {
+                        "value": 500,
+                        "unit": "MHz"
+                    }
+                },
+                "gfx_1": {
+                    "clk": {
+                        "value": 1498,
+                        "unit": "MHz"
+                    }
+                }
+            }
+        }
+    ]
+}"""
+
+
+def test_parse_amd_smi_metric():
+    assert bench.parse_amd_smi_metric(AMD_SMI_SAMPLE) == (1397, [1558, 1498])
+    assert bench.parse_amd_smi_metric("") == (None, [])
+    assert bench.parse_amd_smi_metric("command not found") == (None, [])
+
+
+def test_extra_records_name_the_two_roofline_configs():
+    """The extra records of the default run are the two other configurations
+    with a roofline target: 4096^3 against the MFMA peak, the skinny shape
+    against HBM."""
+    assert bench.EXTRA_RECORDS == ("gemm_4096_f16_quarter", "skinny_16x16384x16384_bf16")
+    for name in bench.EXTRA_RECORDS:
+        w = workloads.WORKLOADS[name]
+        hbm = w.flops / w.algorithmic_bytes < bench.RIDGE_FLOP_PER_BYTE
+        assert hbm == (name.startswith("skinny"))
