@@ -547,6 +547,8 @@ def main():
                 torch.cuda.synchronize()
                 us = e0.elapsed_time(e1) * 1e3 / 10
                 context[key] = {"us": round(us, 1), "tflops": round(w.flops / us / 1e6, 1)}
+                if args.power and key == "bf16_out":
+                    context[key]["power"] = power_sample(fn, torch)
             except (RuntimeError, TypeError) as e:
                 context[key] = f"unavailable: {str(e)[:80]}"
         log(f"[bench] context: {context}")

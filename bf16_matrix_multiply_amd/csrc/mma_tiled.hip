@@ -4,56 +4,60 @@
 // mma_direct.hip (mma.sync page of the TVM tirx docs: "Operand coordinates and
 // ownership"; "Accumulation, transpose and alpha/beta").
 //
-// Instruction: v_mfma_f32_32x32x16_{bf16,f16}. Measured on MI355X with one
-// wave per SIMD, a stream of independent 32x32x16 operations issues at its
-// full 32 cycles each (2.2 PFLOP/s chip-wide), while 16x16x32 operations
-// issue only every ~27 cycles for 16 cycles of work (1.4 PFLOP/s); at two
-// waves per SIMD (this kernel) the 32-wide form still leads, 2.29 against
-// 2.04 PFLOP/s.
+// Macro tiles (TM x TN of D) and their schedules:
+// - 256 x 256 and 256 x 128: 8 waves (two per SIMD) in two groups that
+//   alternate ("ping-pong", below), v_mfma_f32_16x16x32_{bf16,f16};
+// - 128 x 128: 4 waves (two workgroups per CU), one group, v_mfma_f32_32x32x16.
 //
-// Fragment map (B fed as the first operand, A as the second, so the result is
-// D transposed): lane l supplies row n = l % 32 of a 32-column block of B and
-// row m = l % 32 of a 32-row block of A, each with the 8 K values of chunk
-// l / 32 of the operation's 16 (half of one k = 16 atom, or one whole k = 8
-// atom). It receives 16 floats:
-// register r = 4q + t holds D[m = l % 32][n = 8q + 4 * (l / 32) + t], i.e.
-// for each q one contiguous 16-byte piece of N atom q of the block.
+// Why 16x16x32 in the ping-pong path: at 8192^3 on normal(0,1) bf16 operands
+// the chip runs at its 1400 W power limit, so speed is set by energy per flop.
+// Per flop, 16x16x32 reads and writes half the accumulator registers of
+// 32x32x16 (4 + 4 per 8192 products against 16 + 16 per 16384), for the same
+// LDS bytes. Measured on MI355X in one process: 8192^3 803.3 -> 760.0 us,
+// 8192^3 on quarter-integer operands 719.5 -> 674.9 us, 4096^3 88.8 -> 84.0 us,
+// with the same bits: each 16x16x32 step sums the same 32 products per output
+// into the same accumulator as two 32x32x16 steps.
 //
-// Macro tile 256 (M) x 256 (N), 8 waves (two per SIMD) in a 2 x 4 grid, each
-// wave owning a 128 x 64 block of D = 4 x 2 blocks of 32 x 32 (8 accumulators
-// of 16 floats per lane, 128 registers). K advances in slabs of 32 values
-// (four 8-value chunks: 2 atoms of k = 16 or 4 of k = 8).
+// 16x16x32 fragment map (B fed as the first operand, A as the second, so the
+// result is D transposed): lane l supplies row n = l % 16 of a 16-column block
+// of B and row m = l % 16 of a 16-row block of A, each with the 8 K values of
+// chunk l / 16 of the 32-deep step (k = 16 layout: atom chunk / 2, half
+// chunk % 2; k = 8 layout: atom chunk), and receives
+// D[m = l % 16][n = 4 * (l / 16) .. + 3]: one contiguous 16-byte piece of an
+// accumulator atom.
+// 32x32x16 fragment map (128 x 128 tile): lane l supplies row l % 32 of a
+// 32-column block of B and of a 32-row block of A with the 8 K values of chunk
+// l / 32 of a 16-deep half step, and register r = 4q + t receives
+// D[m = l % 32][n = 8q + 4 * (l / 32) + t].
 //
-// Staging takes the role the pages give to TMA box loads ("cp.async.bulk.
-// tensor" page). The LDS image of a slab is fragment-major: 16 A fragments
-// (8 row blocks x 2 K halves) and 16 B fragments of 1 KB each, every fragment
-// stored in lane order, so one direct-to-LDS buffer load (each lane's 16
-// bytes land at M0 + 16 * lane) writes exactly one fragment, gathered from
-// two A atoms or four B atoms in HBM, and one ds_read_b128 per lane reads it
-// back contiguously (no bank conflicts). Loads run four slabs deep: a ring of
-// four 32 KB stages, with slab s+4 loaded into the stage slab s has just left.
-// Rows past M_rep / N_rep read as zero through the buffer range check and K
-// chunks past the end are given an out-of-range offset, so the loop has no
-// branches; slabs past the end load as zeros and are multiplied harmlessly.
-// A second grid axis, when present, splits K (split-K form, below).
+// K advances in slabs of 32 values (four 8-value chunks: 2 atoms of k = 16 or
+// 4 of k = 8). Staging takes the role the pages give to TMA box loads
+// ("cp.async.bulk.tensor" page). The LDS image of a slab is fragment-major:
+// every 1 KB holds one operand fragment in lane order, so one direct-to-LDS
+// buffer load (each lane's 16 bytes land at M0 + 16 * lane) writes exactly one
+// fragment, gathered from the packed atoms in HBM, and one ds_read_b128 per
+// lane reads it back contiguously (no bank conflicts). Loads run four slabs
+// deep: a ring of four stages, with slab s+4 loaded into the stage slab s has
+// just left. Rows past M_rep / N_rep read as zero through the buffer range
+// check and K chunks past the end are given an out-of-range offset, so the
+// loop has no branches; slabs past the end load as zeros and are multiplied
+// harmlessly. A second grid axis, when present, splits K (split-K form).
 //
-// Schedule of the 256 x 256 tile ("ping-pong"): waves 0-3 (group 0, the upper
-// 128 rows) and waves 4-7 (group 1, the lower 128 rows) share the four SIMDs,
-// one wave of each per SIMD. Every slab has two phases, each ended by a
-// workgroup barrier. In phase 0 group 0 issues the 16 MFMAs of the slab
-// back to back while group 1 reads its fragments of the slab from LDS and
-// issues its loads of slab t+3; in phase 1 the roles swap (group 1 multiplies,
-// group 0 reads its fragments of slab t+1 and issues its loads of slab t+4).
-// So on every SIMD one wave keeps the MFMA pipe busy while the other does the
-// memory work and waits, and at a barrier the waiting wave starts its MFMAs
-// while the last ones of the other wave drain. Both groups run the same
-// number of barriers. Each barrier is a bare s_barrier after a counted wait,
-// so loads of later slabs stay in flight across it.
+// Ping-pong schedule (256 x 256: each wave owns 128 x 64 of D; 256 x 128: 64 x
+// 64): waves 0-3 (group 0, the upper 128 rows) and waves 4-7 (group 1, the
+// lower 128 rows) share the four SIMDs, one wave of each per SIMD. Every slab
+// has two phases, each ended by a workgroup barrier. In phase 0 group 0 issues
+// the slab's MFMAs back to back while group 1 reads its fragments of the slab
+// from LDS and issues its loads of slab t+3; in phase 1 the roles swap (group
+// 1 multiplies, group 0 reads its fragments of slab t+1 and issues its loads
+// of slab t+4). So on every SIMD one wave keeps the MFMA pipe busy while the
+// other does the memory work and waits, and at a barrier the waiting wave
+// starts its MFMAs while the last ones of the other wave drain. Both groups
+// run the same number of barriers. Each barrier is a bare s_barrier after a
+// counted wait, so loads of later slabs stay in flight across it.
 //
-// The 256 x 128 tile runs the same ping-pong schedule with its 8 waves in a
-// 4 x 2 grid of 64 x 64 blocks (three loads per wave per slab). The 128 x 128
-// tile (two workgroups per CU, one wave per SIMD each) keeps a one-group
-// schedule: per slab, the MFMAs of the first 16-value half on
+// The 128 x 128 tile (two workgroups per CU, one wave per SIMD each) keeps a
+// one-group schedule: per slab, the MFMAs of the first 16-value half on
 // fragments already in registers; wait for its own loads of the next slab and
 // its fragment reads; barrier; issue the loads of slab s+4; read the next
 // slab's fragments; the MFMAs of the second half.
@@ -83,7 +87,8 @@ namespace {
 //   chip but enough of these;
 // - 128 x 128: 4 waves in a 2 x 2 grid, each 64 x 64, a 64 KB ring, two
 //   workgroups per CU.
-// Every wave covers 64 columns (two 32-column blocks).
+// Every wave covers 64 columns. kWaveBlocksM/N count 32-row / 32-column
+// blocks per wave; a stage holds TM / 16 A and TN / 16 B fragments of 1 KB.
 template <int TM, int TN>
 struct Tile {
   static constexpr int kWaves = TM == 256 ? 8 : 4;
@@ -193,12 +198,19 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
   const int64_t m_atom0 = tc.mt * kTileMAtoms, n_atom0 = tc.nt * kTileNAtoms;
 
   // ---- direct-to-LDS staging ----
-  // Wave w loads A fragments f = 8r + w (row block f / 2, 16-deep half f % 2 =
-  // w % 2 of the slab) and B fragments likewise. Lane l of an A fragment
-  // fetches row l % 16 of M atom 2 * (f / 2) + (l / 16) % 2, and of a B
-  // fragment row l % 8 of N atom 4 * (f / 2) + (l / 8) % 4; in both, the 8 K
-  // values of chunk cs = 2 * (f % 2) + l / 32 of the slab's four 8-value
-  // chunks (k = 16 layout: atom cs / 2, half cs % 2; k = 8 layout: atom cs).
+  // Wave w loads fragments f = 8r + w of A and of B (f = 4r + w for the
+  // 4-wave tile), one 1 KB fragment per load.
+  // - 16x16x32 (8 waves): A fragment f is M atom f, 16 rows x 32 K values
+  //   (two adjacent K atoms: 1 KB contiguous in HBM); B fragment f is N atoms
+  //   2f and 2f + 1, 16 columns x 32 K. Lane l fetches row l % 16 (B: row l % 8
+  //   of N atom 2f + (l / 8) % 2) with the 8 K values of chunk l / 16.
+  // - 32x32x16 (4 waves): fragment f covers 32-row block f / 2 and the
+  //   16-deep half f % 2 = w % 2 of the slab. Lane l of an A fragment fetches
+  //   row l % 16 of M atom 2 * (f / 2) + (l / 16) % 2, and of a B fragment row
+  //   l % 8 of N atom 4 * (f / 2) + (l / 8) % 4; in both, the 8 K values of
+  //   chunk cs = 2 * (f % 2) + l / 32 of the slab's four 8-value chunks.
+  // In both maps a chunk is atom chunk / 2, half chunk % 2 of the k = 16
+  // layout, or atom chunk of the k = 8 layout.
   const int kj = wave & 1;
   const int cs = 2 * kj + (lane >> 5);
   const int64_t nck = k_chunks(p);
@@ -228,27 +240,46 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
   constexpr int kMaxLoads = 2;
   static_assert(kLoadsA <= kMaxLoads && kLoadsB <= kMaxLoads, "offset arrays too small");
   uint32_t a_voff[kMaxLoads], b_voff[kMaxLoads];
+  constexpr bool kM16 = kWaves == 8;   // the ping-pong path multiplies with 16x16x32
+  const int g16 = lane >> 4;           // its lanes' 8-value chunk of the slab
+  if constexpr (kM16) {
 #pragma unroll
-  for (int r = 0; r < kLoadsA; ++r) {
-    const int blk = (kWaves * r + wave) >> 1;
-    a_voff[r] = uint32_t((2 * blk + ((lane >> 4) & 1)) * a_row_bytes +
-                         (KA == 16 ? kj * 512 + (lane & 15) * 32 + (lane >> 5) * 16
-                                         : cs * 256 + (lane & 15) * 16));
-  }
+    for (int r = 0; r < kLoadsA; ++r) {
+      const int f = kWaves * r + wave;
+      a_voff[r] = uint32_t(f * a_row_bytes +
+                           (KA == 16 ? (g16 >> 1) * 512 + (lane & 15) * 32 + (g16 & 1) * 16
+                                     : g16 * 256 + (lane & 15) * 16));
+    }
 #pragma unroll
-  for (int r = 0; r < kLoadsB; ++r) {
-    const int blk = (kWaves * r + wave) >> 1;
-    b_voff[r] = uint32_t((4 * blk + ((lane >> 3) & 3)) * b_row_bytes +
-                         (KA == 16 ? kj * 256 + (lane & 7) * 32 + (lane >> 5) * 16
-                                         : cs * 128 + (lane & 7) * 16));
+    for (int r = 0; r < kLoadsB; ++r) {
+      const int f = kWaves * r + wave;
+      b_voff[r] = uint32_t((2 * f + ((lane >> 3) & 1)) * b_row_bytes +
+                           (KA == 16 ? (g16 >> 1) * 256 + (lane & 7) * 32 + (g16 & 1) * 16
+                                     : g16 * 128 + (lane & 7) * 16));
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kLoadsA; ++r) {
+      const int blk = (kWaves * r + wave) >> 1;
+      a_voff[r] = uint32_t((2 * blk + ((lane >> 4) & 1)) * a_row_bytes +
+                           (KA == 16 ? kj * 512 + (lane & 15) * 32 + (lane >> 5) * 16
+                                     : cs * 256 + (lane & 15) * 16));
+    }
+#pragma unroll
+    for (int r = 0; r < kLoadsB; ++r) {
+      const int blk = (kWaves * r + wave) >> 1;
+      b_voff[r] = uint32_t((4 * blk + ((lane >> 3) & 3)) * b_row_bytes +
+                           (KA == 16 ? kj * 256 + (lane & 7) * 32 + (lane >> 5) * 16
+                                     : cs * 128 + (lane & 7) * 16));
+    }
   }
 
   // Loads of slab k into stage st (slabs past the end, and K chunks past it,
-  // read 0). With k = 16 atoms both halves of an atom are valid together, so
-  // the test is uniform over the wave.
+  // read 0). With k = 16 atoms both halves of an atom are valid together; in
+  // the 32x32x16 map the test is then uniform over the wave.
   auto issue = [&](Stage& st, int64_t k) {
     const uint32_t koff_a = uint32_t(k * 1024), koff_b = uint32_t(k * 512);
-    const bool k_ok = KA == 16 ? 4 * k + 2 * kj < kcn : 4 * k + cs < kcn;
+    const bool k_ok = kM16 ? 4 * k + g16 < kcn : KA == 16 ? 4 * k + 2 * kj < kcn : 4 * k + cs < kcn;
 #pragma unroll
     for (int r = 0; r < kLoadsA; ++r)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -261,100 +292,76 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
           k_ok ? b_voff[r] : kOutOfRange, koff_b, 0, 0);
   };
 
-  // ---- accumulators: C (read once, here) or the scalar ----
-  // Block (pm, qn) of the wave: rows 32 * (4 wm + pm) .. +31, columns
-  // 32 * (2 wn + qn) .. +31 of the tile. Lane l, register 4q + t: row l % 32,
-  // column 8q + 4 (l / 32) + t of the block.
-  f32x16 acc[kWaveBlocksM][kWaveBlocksN];
-  const int64_t lane_row_atom = m_atom0 + 2 * (kWaveBlocksM * wm) + ((lane >> 4) & 1);  // + 2 pm
-  const int64_t lane_col_atom = n_atom0 + 4 * (kWaveBlocksN * wn);                     // + 4 qn + q
-  const bool interior = m_atom0 + kTileMAtoms <= p.M_rep && n_atom0 + kTileNAtoms <= p.N_rep;
-  const int64_t d_lane =
-      (((tc.b * p.M_rep + lane_row_atom) * p.N_rep + lane_col_atom) * 16 + (lane & 15)) * 8 +
-      4 * (lane >> 5);
-  const int64_t d_mstride = p.N_rep * kAtomFloats;  // next M atom
-  auto init_acc = [&]() {
-    if constexpr (kScaled) {
-      // alpha/beta form: the product starts from zero, C is read in the epilogue
+  if constexpr (kM16) {
+    // ---- two groups in ping-pong, 16x16x32 (schedule above) ----
+    // Wave (wm, wn) owns 16-row blocks pm and 16-column blocks qn of D; lane l
+    // carries row l % 16 of each block and its columns 4 * (l / 16) .. + 3:
+    // one 16-byte piece of one accumulator atom per block.
+    constexpr int kBM = T::kWaveBlocksM * 2, kBN = 4;   // 16-row / 16-column blocks per wave
+    f32x4 acc[kBM][kBN];
+    const int64_t lane_row_atom = m_atom0 + kBM * wm;                      // + pm
+    const int64_t lane_col_atom = n_atom0 + 2 * kBN * wn + (g16 >> 1);     // + 2 qn
+    const bool interior = m_atom0 + kTileMAtoms <= p.M_rep && n_atom0 + kTileNAtoms <= p.N_rep;
+    const int64_t d_lane =
+        (((tc.b * p.M_rep + lane_row_atom) * p.N_rep + lane_col_atom) * 16 + (lane & 15)) * 8 +
+        4 * (g16 & 1);
+    const int64_t d_mstride = p.N_rep * kAtomFloats;  // next M atom
+    auto init_acc = [&]() {
+      if constexpr (kScaled) {
 #pragma unroll
-      for (int pm = 0; pm < kWaveBlocksM; ++pm)
+        for (int pm = 0; pm < kBM; ++pm)
 #pragma unroll
-        for (int qn = 0; qn < kWaveBlocksN; ++qn) acc[pm][qn] = f32x16{};
-    } else if constexpr (kHasC) {
-      auto set4 = [&](int pm, int qn, int q, f32x4 v) {
-        acc[pm][qn][4 * q + 0] = v[0];
-        acc[pm][qn][4 * q + 1] = v[1];
-        acc[pm][qn][4 * q + 2] = v[2];
-        acc[pm][qn][4 * q + 3] = v[3];
-      };
-      if (interior) {
-        // one lane address; the pieces differ by constants and a uniform stride
-        const float* cl = p.C + d_lane;
+          for (int qn = 0; qn < kBN; ++qn) acc[pm][qn] = f32x4{0.f, 0.f, 0.f, 0.f};
+      } else if constexpr (kHasC) {
+        if (interior) {
+          const float* cl = p.C + d_lane;
 #pragma unroll
-        for (int pm = 0; pm < kWaveBlocksM; ++pm)
+          for (int pm = 0; pm < kBM; ++pm)
 #pragma unroll
-          for (int qn = 0; qn < kWaveBlocksN; ++qn)
+            for (int qn = 0; qn < kBN; ++qn)
+              acc[pm][qn] = load16f_nt(cl + pm * d_mstride + 2 * qn * kAtomFloats);
+        } else {
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              set4(pm, qn, q, load16f_nt(cl + 2 * pm * d_mstride + (4 * qn + q) * kAtomFloats));
-      } else {
-        // Blocks outside a ragged last tile read a clamped (valid) address:
-        // their accumulators are never stored.
+          for (int pm = 0; pm < kBM; ++pm)
 #pragma unroll
-        for (int pm = 0; pm < kWaveBlocksM; ++pm)
-#pragma unroll
-          for (int qn = 0; qn < kWaveBlocksN; ++qn)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int64_t ra = lane_row_atom + 2 * pm, ca = lane_col_atom + 4 * qn + q;
+            for (int qn = 0; qn < kBN; ++qn) {
+              const int64_t ra = lane_row_atom + pm, ca = lane_col_atom + 2 * qn;
               const int64_t ma = ra < p.M_rep ? ra : p.M_rep - 1;
               const int64_t na = ca < p.N_rep ? ca : p.N_rep - 1;
-              set4(pm, qn, q, load16f_nt(p.C + (((tc.b * p.M_rep + ma) * p.N_rep + na) * 16 +
-                                                (lane & 15)) * 8 + 4 * (lane >> 5)));
+              acc[pm][qn] = load16f_nt(p.C + (((tc.b * p.M_rep + ma) * p.N_rep + na) * 16 +
+                                              (lane & 15)) * 8 + 4 * (g16 & 1));
             }
+        }
+      } else {
+#pragma unroll
+        for (int pm = 0; pm < kBM; ++pm)
+#pragma unroll
+          for (int qn = 0; qn < kBN; ++qn)
+            acc[pm][qn] = f32x4{p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
       }
-    } else {
-#pragma unroll
-      for (int pm = 0; pm < kWaveBlocksM; ++pm)
-#pragma unroll
-        for (int qn = 0; qn < kWaveBlocksN; ++qn)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[pm][qn][e] = p.c_scalar;
-    }
-  };
-
-  auto sync = [&]() {
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
-  };
-  const int64_t n_slabs = (kcn + 3) / 4;
-
-  if constexpr (kWaves == 8) {
-    // ---- two groups in ping-pong (schedule above) ----
-    // All fragments of one slab for this wave: [K half][B blocks, then A blocks].
-    u32x4 F[2][kWaveBlocksN + kWaveBlocksM];
+    };
+    auto sync = [&]() {
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+    };
+    const int64_t n_slabs = (kcn + 3) / 4;
+    u32x4 F[kBN + kBM];   // this wave's fragments of one slab: B blocks, then A blocks
     auto read_slab = [&](const Stage& st) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+      for (int i = 0; i < kBN; ++i)
+        F[i] = *(const volatile lds_u32x4*)&st.b[kBN * wn + i][lane];
 #pragma unroll
-        for (int i = 0; i < kWaveBlocksN; ++i)
-          F[j][i] = *(const volatile lds_u32x4*)&st.b[2 * (kWaveBlocksN * wn + i) + j][lane];
-#pragma unroll
-        for (int i = 0; i < kWaveBlocksM; ++i)
-          F[j][kWaveBlocksN + i] =
-              *(const volatile lds_u32x4*)&st.a[2 * (kWaveBlocksM * wm + i) + j][lane];
-      }
+      for (int i = 0; i < kBM; ++i)
+        F[kBN + i] = *(const volatile lds_u32x4*)&st.a[kBM * wm + i][lane];
     };
     auto mfma_slab = [&]() {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+      for (int pm = 0; pm < kBM; ++pm)
 #pragma unroll
-        for (int pm = 0; pm < kWaveBlocksM; ++pm)
-#pragma unroll
-          for (int qn = 0; qn < kWaveBlocksN; ++qn)
-            acc[pm][qn] = mfma_32x32x16<DT>(F[j][qn], F[j][kWaveBlocksN + pm], acc[pm][qn]);
+        for (int qn = 0; qn < kBN; ++qn)
+          acc[pm][qn] = mfma_16x16x32<DT>(F[qn], F[kBN + pm], acc[pm][qn]);
     };
     // Ring invariant: a group's own loads of a slab are waited for (counted
     // vmcnt) in its memory phase two slabs before the slab is read, and the
@@ -413,87 +420,17 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
         slab(s + 3, st2, st3);
       }
     }
-  } else {
-    // ---- one group (128 x 128 tile) ----
-    init_acc();
-    // Slabs 0..3 into the ring; C (issued first) and slab 0 must have landed.
-    issue(st0, 0);
-    issue(st1, 1);
-    issue(st2, 2);
-    issue(st3, 3);
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoadsPerSlab, 15));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("" ::: "memory");
+    // No load may still be writing LDS when the workgroup ends.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-    // Fragments of one slab: [K half][block]. Reads are volatile LDS loads so
-    // they stay where they are written (a half slab ahead of their MFMAs)
-    // instead of being sunk to their first use.
-    using FragB = u32x4[2][kWaveBlocksN];
-    using FragA = u32x4[2][kWaveBlocksM];
-    FragB fb[2];
-    FragA fa[2];
-    auto read_frags = [&](const Stage& st, FragB& b, FragA& a) {
+    // ---- epilogue: one 16-byte store per block ----
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
+    for (int pm = 0; pm < kBM; ++pm)
 #pragma unroll
-        for (int i = 0; i < kWaveBlocksN; ++i)
-          b[j][i] = *(const volatile lds_u32x4*)&st.b[2 * (kWaveBlocksN * wn + i) + j][lane];
-#pragma unroll
-        for (int i = 0; i < kWaveBlocksM; ++i)
-          a[j][i] = *(const volatile lds_u32x4*)&st.a[2 * (kWaveBlocksM * wm + i) + j][lane];
-      }
-    };
-    auto mfma_katom = [&](const u32x4 (&b)[kWaveBlocksN], const u32x4 (&a)[kWaveBlocksM]) {
-#pragma unroll
-      for (int pm = 0; pm < kWaveBlocksM; ++pm)
-#pragma unroll
-        for (int qn = 0; qn < kWaveBlocksN; ++qn)
-          acc[pm][qn] = mfma_32x32x16<DT>(b[qn], a[pm], acc[pm][qn]);
-    };
-
-    read_frags(st0, fb[0], fa[0]);
-
-    auto slab = [&](int64_t s, Stage& cur, const Stage& nxt, FragB& bc, FragA& ac, FragB& bn,
-                    FragA& an) {
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_katom(bc[0], ac[0]);
-      // own loads of slab s+1 landed (slabs s+2, s+3 may still be in flight);
-      // own fragment reads of this stage done
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsPerSlab, 0));
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("" ::: "memory");
-      issue(cur, s + kStages);
-      read_frags(nxt, bn, an);
-      mfma_katom(bc[1], ac[1]);
-      // The compiler interleaves these: the MFMAs of the second K half go
-      // first, so the pipe has work right after the barrier, with the loads of
-      // slab s+4 and the next slab's fragment reads spread among them.
-    };
-    const int64_t n_slabs = (kcn + 3) / 4;
-    for (int64_t s = 0; s < n_slabs; s += kStages) {
-      slab(s + 0, st0, st1, fb[0], fa[0], fb[1], fa[1]);
-      slab(s + 1, st1, st2, fb[1], fa[1], fb[0], fa[0]);
-      slab(s + 2, st2, st3, fb[0], fa[0], fb[1], fa[1]);
-      slab(s + 3, st3, st0, fb[1], fa[1], fb[0], fa[0]);
-    }
-  }
-  // No load may still be writing LDS when the workgroup ends.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-
-  // ---- epilogue: per block, four 16-byte stores (one per N atom) ----
-#pragma unroll
-  for (int pm = 0; pm < kWaveBlocksM; ++pm)
-#pragma unroll
-    for (int qn = 0; qn < kWaveBlocksN; ++qn)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        f32x4 v = {acc[pm][qn][4 * q + 0], acc[pm][qn][4 * q + 1], acc[pm][qn][4 * q + 2],
-                   acc[pm][qn][4 * q + 3]};
-        float* dst = Dout + d_lane + 2 * pm * d_mstride + (4 * qn + q) * kAtomFloats;
-        const bool ok =
-            interior || (lane_row_atom + 2 * pm < p.M_rep && lane_col_atom + 4 * qn + q < p.N_rep);
+      for (int qn = 0; qn < kBN; ++qn) {
+        f32x4 v = acc[pm][qn];
+        float* dst = Dout + d_lane + pm * d_mstride + 2 * qn * kAtomFloats;
+        const bool ok = interior || (lane_row_atom + pm < p.M_rep && lane_col_atom + 2 * qn < p.N_rep);
         if constexpr (kScaled) {
           f32x4 cv = {p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
           if constexpr (kHasC) {
@@ -509,6 +446,164 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
             store16f_nt(dst, v);
         }
       }
+  } else {
+  // ---- accumulators: C (read once, here) or the scalar ----
+    // Block (pm, qn) of the wave: rows 32 * (4 wm + pm) .. +31, columns
+    // 32 * (2 wn + qn) .. +31 of the tile. Lane l, register 4q + t: row l % 32,
+    // column 8q + 4 (l / 32) + t of the block.
+    f32x16 acc[kWaveBlocksM][kWaveBlocksN];
+    const int64_t lane_row_atom = m_atom0 + 2 * (kWaveBlocksM * wm) + ((lane >> 4) & 1);  // + 2 pm
+    const int64_t lane_col_atom = n_atom0 + 4 * (kWaveBlocksN * wn);                     // + 4 qn + q
+    const bool interior = m_atom0 + kTileMAtoms <= p.M_rep && n_atom0 + kTileNAtoms <= p.N_rep;
+    const int64_t d_lane =
+        (((tc.b * p.M_rep + lane_row_atom) * p.N_rep + lane_col_atom) * 16 + (lane & 15)) * 8 +
+        4 * (lane >> 5);
+    const int64_t d_mstride = p.N_rep * kAtomFloats;  // next M atom
+    auto init_acc = [&]() {
+      if constexpr (kScaled) {
+        // alpha/beta form: the product starts from zero, C is read in the epilogue
+#pragma unroll
+        for (int pm = 0; pm < kWaveBlocksM; ++pm)
+#pragma unroll
+          for (int qn = 0; qn < kWaveBlocksN; ++qn) acc[pm][qn] = f32x16{};
+      } else if constexpr (kHasC) {
+        auto set4 = [&](int pm, int qn, int q, f32x4 v) {
+          acc[pm][qn][4 * q + 0] = v[0];
+          acc[pm][qn][4 * q + 1] = v[1];
+          acc[pm][qn][4 * q + 2] = v[2];
+          acc[pm][qn][4 * q + 3] = v[3];
+        };
+        if (interior) {
+          // one lane address; the pieces differ by constants and a uniform stride
+          const float* cl = p.C + d_lane;
+#pragma unroll
+          for (int pm = 0; pm < kWaveBlocksM; ++pm)
+#pragma unroll
+            for (int qn = 0; qn < kWaveBlocksN; ++qn)
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                set4(pm, qn, q, load16f_nt(cl + 2 * pm * d_mstride + (4 * qn + q) * kAtomFloats));
+        } else {
+          // Blocks outside a ragged last tile read a clamped (valid) address:
+          // their accumulators are never stored.
+#pragma unroll
+          for (int pm = 0; pm < kWaveBlocksM; ++pm)
+#pragma unroll
+            for (int qn = 0; qn < kWaveBlocksN; ++qn)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const int64_t ra = lane_row_atom + 2 * pm, ca = lane_col_atom + 4 * qn + q;
+                const int64_t ma = ra < p.M_rep ? ra : p.M_rep - 1;
+                const int64_t na = ca < p.N_rep ? ca : p.N_rep - 1;
+                set4(pm, qn, q, load16f_nt(p.C + (((tc.b * p.M_rep + ma) * p.N_rep + na) * 16 +
+                                                  (lane & 15)) * 8 + 4 * (lane >> 5)));
+              }
+        }
+      } else {
+#pragma unroll
+        for (int pm = 0; pm < kWaveBlocksM; ++pm)
+#pragma unroll
+          for (int qn = 0; qn < kWaveBlocksN; ++qn)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[pm][qn][e] = p.c_scalar;
+      }
+    };
+
+    // ---- one group (128 x 128 tile) ----
+      init_acc();
+      // Slabs 0..3 into the ring; C (issued first) and slab 0 must have landed.
+      issue(st0, 0);
+      issue(st1, 1);
+      issue(st2, 2);
+      issue(st3, 3);
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(3 * kLoadsPerSlab, 15));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      asm volatile("" ::: "memory");
+  
+      // Fragments of one slab: [K half][block]. Reads are volatile LDS loads so
+      // they stay where they are written (a half slab ahead of their MFMAs)
+      // instead of being sunk to their first use.
+      using FragB = u32x4[2][kWaveBlocksN];
+      using FragA = u32x4[2][kWaveBlocksM];
+      FragB fb[2];
+      FragA fa[2];
+      auto read_frags = [&](const Stage& st, FragB& b, FragA& a) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+          for (int i = 0; i < kWaveBlocksN; ++i)
+            b[j][i] = *(const volatile lds_u32x4*)&st.b[2 * (kWaveBlocksN * wn + i) + j][lane];
+#pragma unroll
+          for (int i = 0; i < kWaveBlocksM; ++i)
+            a[j][i] = *(const volatile lds_u32x4*)&st.a[2 * (kWaveBlocksM * wm + i) + j][lane];
+        }
+      };
+      auto mfma_katom = [&](const u32x4 (&b)[kWaveBlocksN], const u32x4 (&a)[kWaveBlocksM]) {
+#pragma unroll
+        for (int pm = 0; pm < kWaveBlocksM; ++pm)
+#pragma unroll
+          for (int qn = 0; qn < kWaveBlocksN; ++qn)
+            acc[pm][qn] = mfma_32x32x16<DT>(b[qn], a[pm], acc[pm][qn]);
+      };
+  
+      read_frags(st0, fb[0], fa[0]);
+  
+      auto slab = [&](int64_t s, Stage& cur, const Stage& nxt, FragB& bc, FragA& ac, FragB& bn,
+                      FragA& an) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_katom(bc[0], ac[0]);
+        // own loads of slab s+1 landed (slabs s+2, s+3 may still be in flight);
+        // own fragment reads of this stage done
+        __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * kLoadsPerSlab, 0));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" ::: "memory");
+        issue(cur, s + kStages);
+        read_frags(nxt, bn, an);
+        mfma_katom(bc[1], ac[1]);
+        // The compiler interleaves these: the MFMAs of the second K half go
+        // first, so the pipe has work right after the barrier, with the loads of
+        // slab s+4 and the next slab's fragment reads spread among them.
+      };
+      const int64_t n_slabs = (kcn + 3) / 4;
+      for (int64_t s = 0; s < n_slabs; s += kStages) {
+        slab(s + 0, st0, st1, fb[0], fa[0], fb[1], fa[1]);
+        slab(s + 1, st1, st2, fb[1], fa[1], fb[0], fa[0]);
+        slab(s + 2, st2, st3, fb[0], fa[0], fb[1], fa[1]);
+        slab(s + 3, st3, st0, fb[1], fa[1], fb[0], fa[0]);
+      }
+    // No load may still be writing LDS when the workgroup ends.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  
+    // ---- epilogue: per block, four 16-byte stores (one per N atom) ----
+#pragma unroll
+    for (int pm = 0; pm < kWaveBlocksM; ++pm)
+#pragma unroll
+      for (int qn = 0; qn < kWaveBlocksN; ++qn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4 v = {acc[pm][qn][4 * q + 0], acc[pm][qn][4 * q + 1], acc[pm][qn][4 * q + 2],
+                     acc[pm][qn][4 * q + 3]};
+          float* dst = Dout + d_lane + 2 * pm * d_mstride + (4 * qn + q) * kAtomFloats;
+          const bool ok =
+              interior || (lane_row_atom + 2 * pm < p.M_rep && lane_col_atom + 4 * qn + q < p.N_rep);
+          if constexpr (kScaled) {
+            f32x4 cv = {p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
+            if constexpr (kHasC) {
+              if (ok) cv = load16f_nt(p.C + (dst - Dout));
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.alpha, v[e], p.beta * cv[e]);
+          }
+          if (ok) {
+            if (p.splits > 1)
+              store16f(dst, v);   // partial sums: read back by the reduce right away
+            else
+              store16f_nt(dst, v);
+          }
+        }
+  }
 }
 
 template <int TM, int TN>
