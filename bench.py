@@ -250,7 +250,8 @@ def run_box(args, torch, bmm):
 # The other two configurations with a roofline target, measured in the same
 # run as extra records of the default (headline) line: 4096^3 f16 against the
 # MFMA peak, and the skinny M = 16 shape against HBM (warm, and after a cache
-# flush). Each times the multiply alone with an event pair around every call.
+# flush). Each times the multiply alone: warm calls back to back between one
+# pair of events, flushed calls with an event pair each.
 EXTRA_RECORDS = ("gemm_4096_f16_quarter", "skinny_16x16384x16384_bf16")
 
 
@@ -325,13 +326,15 @@ def multiply_record(name, torch, bmm, steps):
         bmm.mma_tile(A, B, C, c, w.dtype, out=D)
 
     warm_up(call, 5, torch)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    for e in evs:
-        e[0].record(stream)
+    # back to back between one pair of events, as the calls run in a loop (an
+    # event after every call would add its own few microseconds to each)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
         call()
-        e[1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    us = float(np.mean([e[0].elapsed_time(e[1]) for e in evs])) * 1e3
+    us = e0.elapsed_time(e1) * 1e3 / steps
     hbm = w.flops / w.algorithmic_bytes < RIDGE_FLOP_PER_BYTE
     rec = {"workload": w.name, "kernel": f"mma_tile[{kernel}]", "dtype": w.dtype,
            "M": w.M, "N": w.N, "K": w.K, "c": "tensor" if w.c_tensor else "scalar",
@@ -342,6 +345,8 @@ def multiply_record(name, torch, bmm, steps):
     if hbm:
         rec.update({"bound": "hbm", "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "achieved": rec["gbs"], "frac": round(rec["gbs"] / PEAK_HBM_GBS, 4)})
+        # after a flush of L2 and the Infinity Cache: each call needs its own
+        # flush, so each has its own event pair, whose cost it includes
         flush = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
         cold = []
         for _ in range(10):
