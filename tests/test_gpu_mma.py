@@ -270,6 +270,23 @@ def test_largest_k_of_the_tiled_kernels():
     gu.assert_parity_sampled(w, inp, ref, idx=gu.per_tile_indices(w, 32, 32, per_tile=1))
 
 
+def test_ragged_many_tiles_all_tile_shapes():
+    """Two batches of 1232 x 1256 x 1040 (ragged in M, N and K: 5 x 5 tiles of
+    256 x 256 per batch, the last ones partial, and an odd K_rep), quarter
+    integers with C on the quarter grid: the three tile shapes give the same
+    bits, every row and column sum of 16*D equals its int64 closed form, and
+    outputs sampled in every 32 x 32 block equal the oracle's."""
+    w = C(2, 1232, 1256, 1040, "bf16", "quarter", "quarter", c_tensor=True, name="ragged_tiles")
+    inp = workloads.make_inputs(w, seed=8)
+    print(f"[ragged_tiles] {w.batch}x{w.M}x{w.N}x{w.K}", flush=True)
+    outs = {k: gu.gpu_run(w, inp, k)[3] for k in ("tiled", "tiled256x128", "tiled128")}
+    ref = outs["tiled"]
+    for k, D in outs.items():
+        assert np.array_equal(D.view(np.uint32), ref.view(np.uint32)), k
+    gu.assert_quarter_sums(w, inp, ref)
+    gu.assert_parity_sampled(w, inp, ref, idx=gu.per_tile_indices(w, 32, 32, per_tile=1))
+
+
 @pytest.mark.parametrize("shape,kernel", [((2048, 2048, 2048), "auto"),
                                           ((2560, 1536, 4096), "tiled128"),
                                           ((4096, 4096, 4096), "tiled128")])
@@ -293,9 +310,9 @@ def test_mid_size_tiled128_sampled(shape, kernel):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_tile_shapes_bitwise(dtype):
     """Normal data, ragged M and N, an odd K_rep: the 256 x 256, 256 x 128 and
-    128 x 128 tiles each give every 32 x 32 block of D the C value first and
-    then one 32x32x16 MFMA per K atom pair in ascending K, so the three agree
-    bit for bit. The split-K form with a single split forms the partial sum
+    128 x 128 tiles each start every output's accumulator at C and then add
+    the products of each 32-deep K step in ascending K (one 16x16x32 MFMA, or
+    two 32x32x16 half steps), so the three agree bit for bit. The split-K form with a single split forms the partial sum
     from zero and then adds C once, so it gives fl(C + P) with P the product
     that either tile gives for a scalar C of 0."""
     w = C(1, 528, 264, 2064, dtype, c_tensor=True, name=f"tiles_{dtype}")
