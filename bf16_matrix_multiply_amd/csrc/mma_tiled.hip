@@ -5,10 +5,11 @@
 // ownership"; "Accumulation, transpose and alpha/beta").
 //
 // Macro tiles (TM x TN of D) and their schedules:
-// - 256 x 256 without split-K or alpha/beta: 4 waves, one per SIMD, each
-//   128 x 128 of D (mma_tiled4_kernel), v_mfma_f32_16x16x32_{bf16,f16};
-// - 256 x 256 with split-K or alpha/beta, and 256 x 128: 8 waves (two per
-//   SIMD) in two groups that alternate ("ping-pong", below), 16x16x32;
+// - 256 x 256 and 256 x 128 without split-K or alpha/beta: 4 waves, one per
+//   SIMD, each 128 x 128 or 128 x 64 of D (mma_tiled4_kernel),
+//   v_mfma_f32_16x16x32_{bf16,f16};
+// - the same tiles with split-K or alpha/beta: 8 waves (two per SIMD) in two
+//   groups that alternate ("ping-pong", below), 16x16x32;
 // - 128 x 128: 4 waves (two workgroups per CU), one group, v_mfma_f32_32x32x16.
 // All of them give the same bits: each 32-deep step adds the same 32 products
 // per output to the same accumulator, in the same order of steps.
@@ -60,15 +61,18 @@
 // run the same number of barriers. Each barrier is a bare s_barrier after a
 // counted wait, so loads of later slabs stay in flight across it.
 //
-// One wave per SIMD (the plain 256 x 256 tile): a wave's 64 accumulators of 4
-// floats fill the 256 accumulator registers, so it holds a 128 x 128 block and
-// reads a third fewer LDS bytes per MFMA than a ping-pong wave. Alone on its
-// SIMD it keeps the pipe fed by placing the next slab's fragment reads and
-// loads between the MFMAs of the current slab, with one barrier per slab.
-// Measured against the ping-pong schedule on 8192^3 normal bf16 with a C
-// tensor, same bits: 0.1-1.1% faster on three boxes (the chip is at its power
-// limit there); 1.1-2.0% with a scalar C and 1.6-2.4% on 4096^3 quarter-integer
-// operands.
+// One wave per SIMD (the plain 256 x 256 and 256 x 128 tiles): in the 256 x 256
+// tile a wave's 64 accumulators of 4 floats fill the 256 accumulator
+// registers, so it holds a 128 x 128 block and reads a third fewer LDS bytes
+// per MFMA than a ping-pong wave. Alone on its SIMD a wave keeps the pipe fed
+// by placing the next slab's fragment reads and loads between the MFMAs of the
+// current slab, with one barrier per slab. Measured against the ping-pong
+// schedule, same bits: 8192^3 normal bf16 with a C tensor 0.1-1.1% faster on
+// three boxes (the chip is at its power limit there), 1.1-2.0% with a scalar
+// C, 1.6-2.4% on 4096^3 quarter-integer operands; the 256 x 128 tile 7-13%
+// faster (8192 x 1024 x 8192 110.6 against 119.3 us, 2304 x 2048 x 4096 45.8
+// against 52.9 us), where the ping-pong phases of 16 MFMAs per wave left the
+// pipe half idle.
 //
 // The 128 x 128 tile (two workgroups per CU, one wave per SIMD each) keeps a
 // one-group schedule: per slab, the MFMAs of the first 16-value half on
@@ -620,22 +624,25 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
   }
 }
 
-// 256 x 256 tile with one wave per SIMD (no split-K, no alpha/beta): 4 waves
-// in a 2 x 2 grid, each 128 x 128 of D as 8 x 8 blocks of 16 x 16, so 64
-// accumulators of 4 floats (all 256 accumulator registers) per lane, and
-// v_mfma_f32_16x16x32. Fragment maps, LDS image and ring are those of the
-// ping-pong tiles; each wave loads fragments f = 4 r + wave of a slab.
-// Per slab a wave multiplies 8 B and 8 A fragments (16 reads for 64 MFMAs,
-// against 12 for 32 in the ping-pong tiles). The next slab's fragments go to a
-// second register set while the current one is multiplied.
-template <int DT, int KA, bool kHasC>
+// 256 x TN tiles (TN = 256 or 128) with one wave per SIMD (no split-K, no
+// alpha/beta): 4 waves in a 2 x 2 grid, each 128 x TN/2 of D as 8 x TN/32
+// blocks of 16 x 16 (TN = 256: 64 accumulators of 4 floats, all 256
+// accumulator registers; TN = 128: 32), and v_mfma_f32_16x16x32. Fragment
+// maps, LDS image and ring are those of the ping-pong tiles; each wave loads
+// fragments f = 4 r + wave of a slab. Per slab a wave multiplies TN/32 B and 8
+// A fragments (TN = 256: 16 reads for 64 MFMAs, against 12 for 32 in the
+// ping-pong tiles). The next slab's fragments go to a second register set
+// while the current one is multiplied.
+template <int TN, int DT, int KA, bool kHasC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
-  using T = Tile<256, 256>;
-  using St = Stage<256, 256>;
+  using T = Tile<256, TN>;
+  using St = Stage<256, TN>;
   constexpr int kW = 4;                               // waves
   constexpr int kTileMAtoms = T::kTileMAtoms, kTileNAtoms = T::kTileNAtoms;
-  constexpr int kLoads = 8;                           // direct-to-LDS loads per wave per slab
+  constexpr int kBN = TN / 32;                        // 16-column blocks per wave (TN / 2 columns)
+  constexpr int kLoadsB = TN / 64;                    // B fragments a wave loads per slab
+  constexpr int kLoads = 4 + kLoadsB;                 // direct-to-LDS loads per wave per slab
   __shared__ __attribute__((aligned(1024))) St st0, st1, st2, st3;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -656,6 +663,9 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
       const_cast<uint32_t*>(p.B + (tc.b * p.N_rep + n_atom0) * kcn * 32), 0,
       int(b_left < kOutOfRange ? b_left : kOutOfRange), kBufferFlags);
   // 16x16x32 gather offsets, as in the ping-pong tiles.
+  // Fixed sizes here and below (used up to kLoadsB, kBN, kF): arrays sized by a
+  // template argument and captured by a lambda make the host-side compilation
+  // drop the kernel's launch stub without a diagnostic.
   uint32_t a_voff[4], b_voff[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -663,6 +673,10 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
     a_voff[r] = uint32_t(f * a_row_bytes +
                          (KA == 16 ? (g16 >> 1) * 512 + (lane & 15) * 32 + (g16 & 1) * 16
                                    : g16 * 256 + (lane & 15) * 16));
+  }
+#pragma unroll
+  for (int r = 0; r < kLoadsB; ++r) {
+    const int f = kW * r + wave;
     b_voff[r] = uint32_t((2 * f + ((lane >> 3) & 1)) * b_row_bytes +
                          (KA == 16 ? (g16 >> 1) * 256 + (lane & 7) * 32 + (g16 & 1) * 16
                                    : g16 * 128 + (lane & 7) * 16));
@@ -675,17 +689,18 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           a_rsrc, (__attribute__((address_space(3))) void*)&st.a[kW * r + wave][0], 16,
           k_ok ? a_voff[r] : kOutOfRange, koff_a, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          b_rsrc, (__attribute__((address_space(3))) void*)&st.b[kW * r + wave][0], 16,
-          k_ok ? b_voff[r] : kOutOfRange, koff_b, 0, 0);
+      if (r < kLoadsB)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            b_rsrc, (__attribute__((address_space(3))) void*)&st.b[kW * r + wave][0], 16,
+            k_ok ? b_voff[r] : kOutOfRange, koff_b, 0, 0);
     }
   };
 
   // Wave (wm, wn) owns 16-row blocks pm and 16-column blocks qn of D; lane l
   // carries row l % 16 of each block and its columns 4 * (l / 16) .. + 3.
-  f32x4 acc[8][8];
+  f32x4 acc[8][8];                  // [pm][qn], qn < kBN
   const int64_t lane_row_atom = m_atom0 + 8 * wm;                  // + pm
-  const int64_t lane_col_atom = n_atom0 + 16 * wn + (g16 >> 1);    // + 2 qn
+  const int64_t lane_col_atom = n_atom0 + 2 * kBN * wn + (g16 >> 1);   // + 2 qn
   const bool interior = m_atom0 + kTileMAtoms <= p.M_rep && n_atom0 + kTileNAtoms <= p.N_rep;
   const int64_t d_lane =
       (((tc.b * p.M_rep + lane_row_atom) * p.N_rep + lane_col_atom) * 16 + (lane & 15)) * 8 +
@@ -697,13 +712,13 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
 #pragma unroll
       for (int pm = 0; pm < 8; ++pm)
 #pragma unroll
-        for (int qn = 0; qn < 8; ++qn)
+        for (int qn = 0; qn < kBN; ++qn)
           acc[pm][qn] = load16f_nt(cl + pm * d_mstride + 2 * qn * kAtomFloats);
     } else {
 #pragma unroll
       for (int pm = 0; pm < 8; ++pm)
 #pragma unroll
-        for (int qn = 0; qn < 8; ++qn) {
+        for (int qn = 0; qn < kBN; ++qn) {
           const int64_t ra = lane_row_atom + pm, ca = lane_col_atom + 2 * qn;
           const int64_t ma = ra < p.M_rep ? ra : p.M_rep - 1;
           const int64_t na = ca < p.N_rep ? ca : p.N_rep - 1;
@@ -715,7 +730,7 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
 #pragma unroll
     for (int pm = 0; pm < 8; ++pm)
 #pragma unroll
-      for (int qn = 0; qn < 8; ++qn) {
+      for (int qn = 0; qn < kBN; ++qn) {
         // Pinned to accumulator registers one by one: equal starting values
         // would otherwise be merged, and the loop would then copy them.
         f32x4 v = f32x4{p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
@@ -724,15 +739,16 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
       }
   }
 
-  u32x4 F0[16], F1[16];   // one slab's fragments: B blocks 0..7, then A blocks 0..7
+  constexpr int kF = kBN + 8;
+  u32x4 F0[16], F1[16];   // one slab's fragments: B blocks 0..kBN-1, then A blocks 0..7
   auto read_slab = [&](const St& st, u32x4 (&F)[16]) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) F[i] = *(const volatile lds_u32x4*)&st.b[8 * wn + i][lane];
+    for (int i = 0; i < kBN; ++i) F[i] = *(const volatile lds_u32x4*)&st.b[kBN * wn + i][lane];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) F[8 + i] = *(const volatile lds_u32x4*)&st.a[8 * wm + i][lane];
+    for (int i = 0; i < 8; ++i) F[kBN + i] = *(const volatile lds_u32x4*)&st.a[8 * wm + i][lane];
   };
   auto mma = [&](int pm, int qn, const u32x4 (&F)[16]) {
-    acc[pm][qn] = mfma_16x16x32<DT>(F[qn], F[8 + pm], acc[pm][qn]);
+    acc[pm][qn] = mfma_16x16x32<DT>(F[qn], F[kBN + pm], acc[pm][qn]);
   };
   const int64_t n_slabs = (kcn + 3) / 4;
   issue(st0, 0);
@@ -760,18 +776,23 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
     read_slab(st_next, Fn);
     issue(st_load, s + 3);
 #pragma unroll
-    for (int i = 2; i < 64; ++i) mma(i / 8, i % 8, Fc);
+    for (int i = 2; i < 8 * kBN; ++i) mma(i / kBN, i % kBN, Fc);
+    // 256 columns: a read after every second MFMA, then a load after every
+    // third; 128 columns (32 MFMAs, 12 reads): a read after every MFMA.
+    constexpr int kPerRead = TN == 256 ? 2 : 1;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 LDS read
+    for (int i = 0; i < kF; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, kPerRead, 0);   // MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);          // 1 LDS read
     }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // 3 MFMAs
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 vector memory read
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, 62 - 32 - 3 * kLoads, 0);
+    constexpr int kRest = 8 * kBN - 2 - kPerRead * kF - 3 * kLoads;
+    static_assert(kRest >= 0, "the slab's MFMAs cover its reads and loads");
+    if constexpr (kRest > 0) __builtin_amdgcn_sched_group_barrier(0x008, kRest, 0);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(kLoads, 0));   // own slab s+2 landed, Fn read
   };
@@ -787,7 +808,7 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
 #pragma unroll
   for (int pm = 0; pm < 8; ++pm)
 #pragma unroll
-    for (int qn = 0; qn < 8; ++qn) {
+    for (int qn = 0; qn < kBN; ++qn) {
       const bool ok =
           interior || (lane_row_atom + pm < p.M_rep && lane_col_atom + 2 * qn < p.N_rep);
       if (ok) store16f_nt(p.D + d_lane + pm * d_mstride + 2 * qn * kAtomFloats, acc[pm][qn]);
@@ -818,11 +839,11 @@ hipError_t launch_tm(const MmaArgs& a, hipStream_t s) {
   auto kern = a.dtype == kBF16 ? pick_ka(std::integral_constant<int, kBF16>{})
                                : pick_ka(std::integral_constant<int, kF16>{});
   const unsigned splits = a.splits > 1 ? unsigned(a.splits) : 1u;
-  if constexpr (TM == 256 && TN == 256) {
+  if constexpr (TM == 256) {
     if (splits == 1 && !a.scaled) {
       auto pick4 = [&](auto dt, auto ka) {
         constexpr int D = decltype(dt)::value, KA = decltype(ka)::value;
-        return a.C ? mma_tiled4_kernel<D, KA, true> : mma_tiled4_kernel<D, KA, false>;
+        return a.C ? mma_tiled4_kernel<TN, D, KA, true> : mma_tiled4_kernel<TN, D, KA, false>;
       };
       auto pick4_ka = [&](auto dt) {
         return a.atom_k == 16 ? pick4(dt, std::integral_constant<int, 16>{})
