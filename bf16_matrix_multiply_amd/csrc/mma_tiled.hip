@@ -5,12 +5,12 @@
 // ownership"; "Accumulation, transpose and alpha/beta").
 //
 // Macro tiles (TM x TN of D) and their schedules:
-// - 256 x 256 and 256 x 128 without split-K or alpha/beta: 4 waves, one per
-//   SIMD, each 128 x 128 or 128 x 64 of D (mma_tiled4_kernel),
-//   v_mfma_f32_16x16x32_{bf16,f16};
-// - the same tiles with split-K or alpha/beta: 8 waves (two per SIMD) in two
-//   groups that alternate ("ping-pong", below), 16x16x32;
-// - 128 x 128: 4 waves (two workgroups per CU), one group, v_mfma_f32_32x32x16.
+// - without split-K or alpha/beta, every tile: 4 waves in a 2 x 2 grid, each
+//   TM/2 x TN/2 of D (mma_tiled4_kernel), v_mfma_f32_16x16x32_{bf16,f16}; one
+//   workgroup per CU for 256 rows (one wave per SIMD), two for 128 x 128;
+// - with split-K or alpha/beta: 256 x 256 and 256 x 128 run 8 waves (two per
+//   SIMD) in two groups that alternate ("ping-pong", below), 16x16x32; 128 x
+//   128 runs 4 waves (two workgroups per CU), one group, v_mfma_f32_32x32x16.
 // All of them give the same bits: each 32-deep step adds the same 32 products
 // per output to the same accumulator, in the same order of steps.
 //
@@ -61,21 +61,22 @@
 // run the same number of barriers. Each barrier is a bare s_barrier after a
 // counted wait, so loads of later slabs stay in flight across it.
 //
-// One wave per SIMD (the plain 256 x 256 and 256 x 128 tiles): in the 256 x 256
-// tile a wave's 64 accumulators of 4 floats fill the 256 accumulator
-// registers, so it holds a 128 x 128 block and reads a third fewer LDS bytes
-// per MFMA than a ping-pong wave. Alone on its SIMD a wave keeps the pipe fed
-// by placing the next slab's fragment reads and loads between the MFMAs of the
-// current slab, with one barrier per slab. Measured against the ping-pong
-// schedule, same bits: 8192^3 normal bf16 with a C tensor 0.1-1.1% faster on
-// three boxes (the chip is at its power limit there), 1.1-2.0% with a scalar
-// C, 1.6-2.4% on 4096^3 quarter-integer operands; the 256 x 128 tile 7-13%
-// faster (8192 x 1024 x 8192 110.6 against 119.3 us, 2304 x 2048 x 4096 45.8
-// against 52.9 us), where the ping-pong phases of 16 MFMAs per wave left the
-// pipe half idle.
+// 4-wave tiles (no split-K, no alpha/beta): in the 256 x 256 tile a wave's 64
+// accumulators of 4 floats fill the 256 accumulator registers, so it holds a
+// 128 x 128 block and reads a third fewer LDS bytes per MFMA than a ping-pong
+// wave. A wave keeps the pipe fed by placing the next slab's fragment reads and
+// loads between the MFMAs of the current slab, with one barrier per slab.
+// Measured against the earlier schedules, same bits: 8192^3 normal bf16 with a
+// C tensor 0.1-1.1% faster than ping-pong on three boxes (the chip is at its
+// power limit there), 1.1-2.0% with a scalar C, 1.6-2.4% on 4096^3
+// quarter-integer operands; the 256 x 128 tile 7-13% faster than ping-pong
+// (8192 x 1024 x 8192 110.6 against 119.3 us, 2304 x 2048 x 4096 45.8 against
+// 52.9 us), where the ping-pong phases of 16 MFMAs per wave left the pipe half
+// idle; the 128 x 128 tile 5-9% faster than the one-group 32x32x16 schedule
+// (2048^3 23.0 against 25.3 us, 2048 x 2048 x 8192 69.5 against 74.4 us).
 //
-// The 128 x 128 tile (two workgroups per CU, one wave per SIMD each) keeps a
-// one-group schedule: per slab, the MFMAs of the first 16-value half on
+// The 128 x 128 tile with split-K or alpha/beta (two workgroups per CU, one
+// wave per SIMD each) keeps a one-group schedule: per slab, the MFMAs of the first 16-value half on
 // fragments already in registers; wait for its own loads of the next slab and
 // its fragment reads; barrier; issue the loads of slab s+4; read the next
 // slab's fragments; the MFMAs of the second half.
@@ -624,25 +625,27 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
   }
 }
 
-// 256 x TN tiles (TN = 256 or 128) with one wave per SIMD (no split-K, no
-// alpha/beta): 4 waves in a 2 x 2 grid, each 128 x TN/2 of D as 8 x TN/32
-// blocks of 16 x 16 (TN = 256: 64 accumulators of 4 floats, all 256
-// accumulator registers; TN = 128: 32), and v_mfma_f32_16x16x32. Fragment
-// maps, LDS image and ring are those of the ping-pong tiles; each wave loads
-// fragments f = 4 r + wave of a slab. Per slab a wave multiplies TN/32 B and 8
-// A fragments (TN = 256: 16 reads for 64 MFMAs, against 12 for 32 in the
-// ping-pong tiles). The next slab's fragments go to a second register set
-// while the current one is multiplied.
-template <int TN, int DT, int KA, bool kHasC>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// TM x TN tiles without split-K or alpha/beta: 4 waves in a 2 x 2 grid, each
+// TM/2 x TN/2 of D as TM/32 x TN/32 blocks of 16 x 16 (256 x 256: 64
+// accumulators of 4 floats, all 256 accumulator registers; 256 x 128: 32;
+// 128 x 128: 16), and v_mfma_f32_16x16x32. Fragment maps, LDS image and ring
+// are those of the ping-pong tiles; each wave loads fragments f = 4 r + wave
+// of a slab. Per slab a wave multiplies TN/32 B and TM/32 A fragments
+// (256 x 256: 16 reads for 64 MFMAs, against 12 for 32 in the ping-pong
+// tiles). The next slab's fragments go to a second register set while the
+// current one is multiplied. 256-row tiles run one workgroup per CU (one wave
+// per SIMD); 128 x 128 tiles (64 KB of LDS) two.
+template <int TM, int TN, int DT, int KA, bool kHasC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 256 ? 1 : 2, TM == 256 ? 1 : 2)))
 void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
-  using T = Tile<256, TN>;
-  using St = Stage<256, TN>;
+  using T = Tile<TM, TN>;
+  using St = Stage<TM, TN>;
   constexpr int kW = 4;                               // waves
   constexpr int kTileMAtoms = T::kTileMAtoms, kTileNAtoms = T::kTileNAtoms;
+  constexpr int kBM = TM / 32;                        // 16-row blocks per wave (TM / 2 rows)
   constexpr int kBN = TN / 32;                        // 16-column blocks per wave (TN / 2 columns)
-  constexpr int kLoadsB = TN / 64;                    // B fragments a wave loads per slab
-  constexpr int kLoads = 4 + kLoadsB;                 // direct-to-LDS loads per wave per slab
+  constexpr int kLoadsA = TM / 64, kLoadsB = TN / 64; // fragments a wave loads per slab
+  constexpr int kLoads = kLoadsA + kLoadsB;           // direct-to-LDS loads per wave per slab
   __shared__ __attribute__((aligned(1024))) St st0, st1, st2, st3;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -663,12 +666,12 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
       const_cast<uint32_t*>(p.B + (tc.b * p.N_rep + n_atom0) * kcn * 32), 0,
       int(b_left < kOutOfRange ? b_left : kOutOfRange), kBufferFlags);
   // 16x16x32 gather offsets, as in the ping-pong tiles.
-  // Fixed sizes here and below (used up to kLoadsB, kBN, kF): arrays sized by a
+  // Fixed sizes here and below (used up to kLoadsA/B, kBM, kBN, kF): arrays sized by a
   // template argument and captured by a lambda make the host-side compilation
   // drop the kernel's launch stub without a diagnostic.
   uint32_t a_voff[4], b_voff[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < kLoadsA; ++r) {
     const int f = kW * r + wave;
     a_voff[r] = uint32_t(f * a_row_bytes +
                          (KA == 16 ? (g16 >> 1) * 512 + (lane & 15) * 32 + (g16 & 1) * 16
@@ -686,9 +689,10 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
     const bool k_ok = 4 * k + g16 < kcn;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          a_rsrc, (__attribute__((address_space(3))) void*)&st.a[kW * r + wave][0], 16,
-          k_ok ? a_voff[r] : kOutOfRange, koff_a, 0, 0);
+      if (r < kLoadsA)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            a_rsrc, (__attribute__((address_space(3))) void*)&st.a[kW * r + wave][0], 16,
+            k_ok ? a_voff[r] : kOutOfRange, koff_a, 0, 0);
       if (r < kLoadsB)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             b_rsrc, (__attribute__((address_space(3))) void*)&st.b[kW * r + wave][0], 16,
@@ -698,8 +702,8 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
 
   // Wave (wm, wn) owns 16-row blocks pm and 16-column blocks qn of D; lane l
   // carries row l % 16 of each block and its columns 4 * (l / 16) .. + 3.
-  f32x4 acc[8][8];                  // [pm][qn], qn < kBN
-  const int64_t lane_row_atom = m_atom0 + 8 * wm;                  // + pm
+  f32x4 acc[8][8];                  // [pm][qn], pm < kBM, qn < kBN
+  const int64_t lane_row_atom = m_atom0 + kBM * wm;                // + pm
   const int64_t lane_col_atom = n_atom0 + 2 * kBN * wn + (g16 >> 1);   // + 2 qn
   const bool interior = m_atom0 + kTileMAtoms <= p.M_rep && n_atom0 + kTileNAtoms <= p.N_rep;
   const int64_t d_lane =
@@ -710,13 +714,13 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
     if (interior) {
       const float* cl = p.C + d_lane;
 #pragma unroll
-      for (int pm = 0; pm < 8; ++pm)
+      for (int pm = 0; pm < kBM; ++pm)
 #pragma unroll
         for (int qn = 0; qn < kBN; ++qn)
           acc[pm][qn] = load16f_nt(cl + pm * d_mstride + 2 * qn * kAtomFloats);
     } else {
 #pragma unroll
-      for (int pm = 0; pm < 8; ++pm)
+      for (int pm = 0; pm < kBM; ++pm)
 #pragma unroll
         for (int qn = 0; qn < kBN; ++qn) {
           const int64_t ra = lane_row_atom + pm, ca = lane_col_atom + 2 * qn;
@@ -728,7 +732,7 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
     }
   } else {
 #pragma unroll
-    for (int pm = 0; pm < 8; ++pm)
+    for (int pm = 0; pm < kBM; ++pm)
 #pragma unroll
       for (int qn = 0; qn < kBN; ++qn) {
         // Pinned to accumulator registers one by one: equal starting values
@@ -739,13 +743,13 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
       }
   }
 
-  constexpr int kF = kBN + 8;
-  u32x4 F0[16], F1[16];   // one slab's fragments: B blocks 0..kBN-1, then A blocks 0..7
+  constexpr int kF = kBN + kBM;
+  u32x4 F0[16], F1[16];   // one slab's fragments: B blocks 0..kBN-1, then A blocks 0..kBM-1
   auto read_slab = [&](const St& st, u32x4 (&F)[16]) {
 #pragma unroll
     for (int i = 0; i < kBN; ++i) F[i] = *(const volatile lds_u32x4*)&st.b[kBN * wn + i][lane];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) F[kBN + i] = *(const volatile lds_u32x4*)&st.a[8 * wm + i][lane];
+    for (int i = 0; i < kBM; ++i) F[kBN + i] = *(const volatile lds_u32x4*)&st.a[kBM * wm + i][lane];
   };
   auto mma = [&](int pm, int qn, const u32x4 (&F)[16]) {
     acc[pm][qn] = mfma_16x16x32<DT>(F[qn], F[kBN + pm], acc[pm][qn]);
@@ -776,10 +780,12 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
     read_slab(st_next, Fn);
     issue(st_load, s + 3);
 #pragma unroll
-    for (int i = 2; i < 8 * kBN; ++i) mma(i / kBN, i % kBN, Fc);
-    // 256 columns: a read after every second MFMA, then a load after every
-    // third; 128 columns (32 MFMAs, 12 reads): a read after every MFMA.
-    constexpr int kPerRead = TN == 256 ? 2 : 1;
+    for (int i = 2; i < kBM * kBN; ++i) mma(i / kBN, i % kBN, Fc);
+    // 256 x 256 (64 MFMAs): a read after every second MFMA, then a load after
+    // every third; 256 x 128 (32 MFMAs): a read after every MFMA, then a load
+    // after every third; 128 x 128 (16 MFMAs): a read, then a load, after every MFMA.
+    constexpr int kPerRead = kBM * kBN >= 64 ? 2 : 1;
+    constexpr int kPerLoad = kBM * kBN >= 32 ? 3 : 1;
 #pragma unroll
     for (int i = 0; i < kF; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, kPerRead, 0);   // MFMAs
@@ -787,10 +793,10 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
     }
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // 3 MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x008, kPerLoad, 0);   // MFMAs
       __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 vector memory read
     }
-    constexpr int kRest = 8 * kBN - 2 - kPerRead * kF - 3 * kLoads;
+    constexpr int kRest = kBM * kBN - 2 - kPerRead * kF - kPerLoad * kLoads;
     static_assert(kRest >= 0, "the slab's MFMAs cover its reads and loads");
     if constexpr (kRest > 0) __builtin_amdgcn_sched_group_barrier(0x008, kRest, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -806,7 +812,7 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
 #pragma unroll
-  for (int pm = 0; pm < 8; ++pm)
+  for (int pm = 0; pm < kBM; ++pm)
 #pragma unroll
     for (int qn = 0; qn < kBN; ++qn) {
       const bool ok =
@@ -839,11 +845,11 @@ hipError_t launch_tm(const MmaArgs& a, hipStream_t s) {
   auto kern = a.dtype == kBF16 ? pick_ka(std::integral_constant<int, kBF16>{})
                                : pick_ka(std::integral_constant<int, kF16>{});
   const unsigned splits = a.splits > 1 ? unsigned(a.splits) : 1u;
-  if constexpr (TM == 256) {
+  {
     if (splits == 1 && !a.scaled) {
       auto pick4 = [&](auto dt, auto ka) {
         constexpr int D = decltype(dt)::value, KA = decltype(ka)::value;
-        return a.C ? mma_tiled4_kernel<TN, D, KA, true> : mma_tiled4_kernel<TN, D, KA, false>;
+        return a.C ? mma_tiled4_kernel<TM, TN, D, KA, true> : mma_tiled4_kernel<TM, TN, D, KA, false>;
       };
       auto pick4_ka = [&](auto dt) {
         return a.atom_k == 16 ? pick4(dt, std::integral_constant<int, 16>{})
