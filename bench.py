@@ -16,7 +16,9 @@ each kernel: the events cost GPU time, so they stay out of the first pass);
 workload on this host's cores. The default (headline) run also adds
 ``extra_records``: the multiply alone on the 4096^3 f16 configuration against
 the MFMA peak, and on the skinny 16 x 16384 x 16384 one against HBM (warm and
-after a cache flush), each with its own traffic record.
+after a cache flush), each with its own traffic record; and ``power``: socket
+power and per-XCD clocks (amd-smi) while the multiply runs back to back for
+3 s, null where amd-smi is missing.
 
     python bench.py --op box_copy|box_store|box_reduce_add
 
@@ -279,8 +281,11 @@ def power_sample(call, torch, seconds=3.0, settle=1.0):
 
     def sampler():
         while not stop[0]:
-            r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True,
-                               text=True)
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"],
+                                   capture_output=True, text=True, timeout=5)
+            except (OSError, subprocess.SubprocessError):
+                continue
             watts, clocks = parse_amd_smi_metric(r.stdout)
             if watts is not None:
                 samples.append((time.perf_counter() - t0, watts, clocks))
@@ -405,7 +410,9 @@ def main():
                          "for context only")
     ap.add_argument("--power", action="store_true",
                     help="also sample socket power and gfx clocks (amd-smi) while the multiply "
-                         "runs back to back for 3 s")
+                         "runs back to back for 3 s (the default headline run always does)")
+    ap.add_argument("--no-power", action="store_true",
+                    help="skip the power sample of the default (headline) run")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra records of the 4096^3 and skinny configurations that "
                          "the default (headline) run adds")
@@ -623,11 +630,11 @@ def main():
     }
     if context is not None:
         line["context"] = context
-    if args.power:
-        line["power"] = power_sample(multiply, torch)
-        log(f"[bench] power while the multiply runs: {line['power']}")
     default_run = (w.name == workloads.HEADLINE and args.kernel == "auto" and not args.kmajor
                    and ka == 16 and splits is None and args.alpha is None and args.beta is None)
+    if args.power or (default_run and not args.no_power):
+        line["power"] = power_sample(multiply, torch)
+        log(f"[bench] power while the multiply runs: {line['power']}")
     if default_run and not args.no_extra:
         line["extra_records"] = {n: multiply_record(n, torch, bmm, args.steps)
                                  for n in EXTRA_RECORDS}
