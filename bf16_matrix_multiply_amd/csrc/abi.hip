@@ -40,23 +40,24 @@ bool direct_fits(int64_t batch, int64_t M_rep, int64_t N_rep) {
 }
 
 // Shape rule of BMM_KERNEL_AUTO (K counted in values), from a sweep of the
-// kernels over shapes from 16 x 1024 x 1024 to 8192^3 on MI355X:
+// kernels over shapes from 16 x 1024 x 1024 to 8192^3 on MI355X (bf16, normal
+// operands, 4-wave tiles):
 // - 256 x 256 LDS tiles when there are more than 128 (3072^3, 144 tiles:
-//   59.6 us against 67.2 with 128 x 128 tiles and 73.7 with 256 x 128). With
+//   59.0 us against 66.8 with 128 x 128 tiles and 73.6 with 256 x 128). With
 //   128 or fewer the large tiles leave half the CUs idle (8192 x 1024 x 8192,
-//   128 tiles: 134.7 us);
-// - 256 x 128 LDS tiles (the same ping-pong schedule, one workgroup per CU)
-//   when there are more than 128 of them (8192 x 1024 x 8192, 256 tiles: 112.3
-//   against 121.7 us with 128 x 128 tiles; 2304 x 2048 x 4096, 144 tiles: 51.0
-//   against 54.9; 2560^3, 200 tiles: 35.9 against 37.8). With 128 of them the
-//   128 x 128 tile wins (2048 x 2048 x 8192: 80.4 against 71.0 us;
-//   1024 x 4096 x 4096: 44.7 against 39.2);
-// - 128 x 128 LDS tiles when there are at least 128 full ones (2048^3: 24.2
-//   us against 28.0 with 256 x 128 and 38.8 with 256 x 256; 1536^3: 18.2
-//   against 21.3 and 31.5);
+//   128 tiles: 136.4 us);
+// - 256 x 128 LDS tiles (one workgroup per CU) when there are more than 128
+//   of them (8192 x 1024 x 8192, 256 tiles: 102.3 against 111.0 us with
+//   128 x 128 tiles; 2304 x 2304 x 4096, 162 tiles: 46.8 against 50.3; 2560^3,
+//   200 tiles: 34.7 against 36.1). With 128 of them the 128 x 128 tile wins
+//   (2048 x 2048 x 8192: 87.2 against 70.7 us; 1024 x 4096 x 4096: 44.8
+//   against 39.0);
+// - 128 x 128 LDS tiles when there are at least 128 full ones (2048^3: 22.8
+//   us against 26.8 with 256 x 128 and 38.6 with 256 x 256; 1536^3: 18.4
+//   against 21.3 and 31.4);
 // - otherwise the K-splitting, B-streaming kernel, fastest or tied for every
-//   shape with fewer tiles (1024 x 1024 x 8192: 41 against 58 us;
-//   256 x 4096 x 4096: 24 against 33 us);
+//   shape with fewer tiles (1024 x 1024 x 8192: 41.0 against 66.6 us;
+//   256 x 4096 x 4096: 23.9 against 36.0 us);
 // - the direct kernel where the others' launch grids would overflow.
 int choose_kernel(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K) {
   const int64_t tiles256 = batch * ((M_rep + 15) / 16) * ((N_rep + 31) / 32);
@@ -320,16 +321,16 @@ int bmm_splitk_default(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_re
   return int(s < 1 ? 1 : s);
 }
 
-// Whether the split-K form beats the plain entry point for a shape, from the
-// sweep of both over 33 shapes (bf16, normal operands; MI355X). Splitting won
+// Whether the split-K form beats the plain entry point for a shape, from a
+// sweep of both over 28 shapes (bf16, normal operands; MI355X). Splitting won
 // exactly where K >= 4096, M >= 32, AUTO would run the skinny or the 128 x 128
-// kernel and the default split count is above one: 1024 x 1024 x 8192 (30.0
-// against 39.7 us), 2048 x 1024 x 4096 (29.1 / 34.0), 256 x 4096 x 4096
-// (22.0 / 24.0), 64 x 8192 x 8192 (27.4 / 43.7), 32 x 16384 x 4096 (26.3 /
-// 28.8), 1024 x 1024 x 65536 (123.3 / 335.1). It lost with K = 2048
-// (512 x 2048 x 2048: 20.2 / 13.1), with M = 16 (16 x 16384 x 16384, where the
-// skinny kernel streams B once: 106.8 / 85.7) and on the 256 x 128 tile
-// (8192 x 1024 x 8192: 121.4 / 112.3).
+// kernel and the default split count is above one: 1024 x 1024 x 8192 (30.1
+// against 41.0 us), 2048 x 1024 x 4096 (30.1 / 36.5), 256 x 4096 x 4096
+// (22.4 / 23.9), 64 x 8192 x 8192 (27.5 / 44.1), 32 x 16384 x 4096 (26.4 /
+// 28.9), 1024 x 1024 x 65536 (113.6 / 337.1), 512 x 512 x 65536 (48.7 /
+// 270.4). It lost with K = 2048 (512 x 2048 x 2048: 20.3 / 13.3), with M = 16
+// (16 x 16384 x 16384, where the skinny kernel streams B once: 105.7 / 87.0)
+// and on the 256 x 128 tile (8192 x 1024 x 8192: 113.9 / 102.3).
 int bmm_splitk_suggested(int64_t batch, int64_t M_rep, int64_t N_rep, int64_t K_rep,
                          int32_t atom_k) {
   const int s = bmm_splitk_default(batch, M_rep, N_rep, K_rep, atom_k);
