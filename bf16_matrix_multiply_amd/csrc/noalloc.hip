@@ -28,17 +28,30 @@ static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
 std::mutex g_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
-// The device address of this device's copy of the array, looked up once per
-// device (with that device current) and kept.
-hipError_t scratch_on_current_device(void** out) {
+// The device address of the array's copy on the device that runs `stream`
+// (the current device for the null stream), looked up once per device with
+// that device current, and kept.
+hipError_t scratch_for_stream(hipStream_t stream, void** out) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
+  const int current = dev;
+  if (stream) {
+    hipDevice_t sd = -1;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return e;
+    dev = int(sd);
+  }
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_mu);
   if (!g_scratch_ptr[dev]) {
+    if (dev != current && (e = hipSetDevice(dev)) != hipSuccess) return e;
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != current) {
+      const hipError_t r = hipSetDevice(current);
+      if (e == hipSuccess) e = r;
+    }
     if (e != hipSuccess) return e;
     if (!p) return hipErrorInvalidSymbol;
     g_scratch_ptr[dev] = p;
@@ -71,7 +84,7 @@ int bmm_mma_tile_splitk_noalloc(float* D, const uint32_t* A, const uint32_t* B, 
     return BMM_ERANGE;
   }
   void* ws = nullptr;
-  const hipError_t e = scratch_on_current_device(&ws);
+  const hipError_t e = scratch_for_stream(static_cast<hipStream_t>(stream), &ws);
   if (e != hipSuccess) {
     bmm::set_last_error(std::string("mma_tile_splitk_noalloc: scratch address: ") +
                         hipGetErrorString(e));

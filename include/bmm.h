@@ -363,9 +363,9 @@ int bmm_mma_tile_splitk(float* D, const uint32_t* A, const uint32_t* B, const fl
  * allocating routine.
  *
  * The partial sums go to a static device array of BMM_NOALLOC_SCRATCH_BYTES
- * (64 MiB) per device, set up on the first call on that device (the current
- * device, which must be the device of `stream`) and held until the process
- * ends. Same arguments, arithmetic, bits and errors as bmm_mma_tile_splitk,
+ * (64 MiB) per device, set up on the first call on that device (the device
+ * of `stream`; the current device for the null stream) and held until the
+ * process ends. Same arguments, arithmetic, bits and errors as bmm_mma_tile_splitk,
  * minus the workspace; a request whose partial sums
  * (bmm_mma_splitk_workspace_bytes) exceed the array returns BMM_ERANGE and
  * launches nothing. Every call on one device shares that device's array, so

@@ -1,9 +1,9 @@
 """The no-allocation split-K entry point (bmm_mma_tile_splitk_noalloc),
 called through the C ABI: its result equals the workspace form's
 (bmm_mma_tile_splitk with the same split count; same kernels, so the same
-bits) on two calls in a row, the second with a smaller input; both also meet
-the oracle's split-K bound. A request beyond the static scratch is refused
-without touching D."""
+bits) on two calls in a row, the second with a smaller input, and on a third
+call on the null stream; the results also meet the oracle's split-K bound.
+A request beyond the static scratch is refused without touching D."""
 import ctypes
 
 import numpy as np
@@ -24,8 +24,8 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _noalloc(L, D, A, B, C, c, w, splits):
-    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+def _noalloc(L, D, A, B, C, c, w, splits, null_stream=False):
+    stream = None if null_stream else ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     return L.bmm_mma_tile_splitk_noalloc(_ptr(D), _ptr(A), _ptr(B), _ptr(C), float(c), w.batch,
                                          w.M_rep, w.N_rep, w.K_rep, 1, 16, splits, stream)
 
@@ -63,6 +63,16 @@ def test_noalloc_equals_workspace_form_on_consecutive_calls():
         assert not np.isnan(got).any(), f"{w.name}: unwritten outputs"
         assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), w.name
         results.append((w, inp, got, splits))
+        last = (A, B, C, c, shape)
+    # A third call on the null stream (the scratch of the current device), the
+    # smaller input again: the same bits.
+    A, B, C, c, shape = last
+    w, _, got_prev, splits = results[-1]
+    D = torch.full(shape, float("nan"), device="cuda")
+    torch.cuda.synchronize()
+    assert _noalloc(L, D, A, B, C, c, w, splits, null_stream=True) == 0, L.bmm_last_error().decode()
+    torch.cuda.synchronize()
+    assert np.array_equal(D.cpu().numpy().view(np.uint32), got_prev.view(np.uint32))
     for w, inp, got, splits in results:
         Ao, Bo = oracle.pack(inp["a"], 16), oracle.pack(inp["b"], 8)
         rng = np.random.default_rng(5)
