@@ -424,8 +424,22 @@ def test_noalloc_binding_requires_out_and_dtype():
         bmm.mma_tile_splitk_noalloc(A, B, None, 0.0, "bf16")
 
 
-# (M, N, K, default split-K us, plain entry point us): the sweep of both forms on
-# MI355X (bf16 normal operands, no C; profiles/kernel_choice_sweep.md).
+# (M, N, K, default split-K us, plain entry point us): the sweeps of both forms on
+# MI355X (bf16 normal operands, no C; profiles/kernel_choice_sweep.md), with the
+# earlier ping-pong tiles and with the 4-wave tiles.
+SWEEP_4WAVE = [(128, 128, 256, 16.0, 12.5), (512, 512, 512, 15.9, 12.4), (1024, 1024, 1024, 15.4, 12.6),
+               (1536, 1536, 1536, 23.6, 18.4), (2048, 2048, 2048, 30.0, 22.8),
+               (2560, 2560, 2560, 46.4, 34.7), (3072, 3072, 3072, 72.4, 59.0),
+               (4096, 4096, 1024, 59.4, 36.1), (4096, 4096, 4096, 119.1, 95.6),
+               (8192, 8192, 8192, 808.9, 758.1), (1024, 1024, 8192, 30.1, 41.0),
+               (2048, 2048, 8192, 77.4, 70.7), (1024, 4096, 4096, 46.0, 39.0),
+               (2048, 1024, 4096, 30.1, 36.5), (1024, 1024, 65536, 113.6, 337.1),
+               (512, 512, 65536, 48.7, 270.4), (16, 1024, 1024, 17.3, 12.6), (64, 2048, 2048, 15.8, 13.7),
+               (256, 4096, 4096, 22.4, 23.9), (512, 2048, 2048, 20.3, 13.3), (64, 8192, 8192, 27.5, 44.1),
+               (32, 16384, 4096, 26.4, 28.9), (16, 16384, 16384, 105.7, 87.0),
+               (8192, 1024, 8192, 113.9, 102.3), (1024, 8192, 8192, 114.5, 102.7),
+               (2304, 2304, 4096, 60.1, 46.8), (3072, 2048, 4096, 63.6, 48.5),
+               (2816, 2816, 4096, 71.3, 54.1)]
 SWEEP = [(128, 128, 256, 16.9, 12.8), (512, 512, 512, 17.2, 13.5), (1024, 1024, 1024, 17.5, 13.5),
          (1536, 1536, 1536, 22.7, 18.2), (2048, 2048, 2048, 30.6, 24.2),
          (2560, 2560, 2560, 47.0, 35.9), (3072, 3072, 3072, 70.8, 59.6),
@@ -443,7 +457,7 @@ SWEEP = [(128, 128, 256, 16.9, 12.8), (512, 512, 512, 17.2, 13.5), (1024, 1024, 
          (2304, 2304, 2304, 41.6, 31.2), (2048, 2560, 8192, 109.0, 87.5)]
 
 
-@pytest.mark.parametrize("M,N,K,split_us,plain_us", SWEEP)
+@pytest.mark.parametrize("M,N,K,split_us,plain_us", SWEEP + SWEEP_4WAVE)
 def test_splitk_suggested_matches_the_sweep(L, M, N, K, split_us, plain_us):
     """bmm_splitk_suggested says to split exactly where the measured default
     split-K form beat the plain entry point, and then gives that split count."""
