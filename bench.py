@@ -301,16 +301,25 @@ def power_sample(call, torch, seconds=3.0, settle=1.0):
     elapsed = time.perf_counter() - t0
     stop[0] = True
     th.join()
+    return summarize_power(samples, settle, elapsed / calls * 1e6)
+
+
+def summarize_power(samples, settle, us_per_call):
+    """The power object from (seconds since start, watts, [MHz per XCD]) samples:
+    medians over the samples taken after ``settle`` seconds; the per-XCD clocks
+    from the samples that list the usual number of XCDs. None without samples."""
     settled = [x for x in samples if x[0] >= settle]
     if not settled:
         return None
     watts = np.array([x[1] for x in settled])
-    clocks = np.array([x[2] for x in settled if x[2]])
+    lengths = [len(x[2]) for x in settled if x[2]]
+    n_xcd = max(set(lengths), key=lengths.count) if lengths else 0
+    clocks = np.array([x[2] for x in settled if n_xcd and len(x[2]) == n_xcd], dtype=np.int64)
     return {"tool": "amd-smi metric -p -c", "samples": len(settled),
             "socket_w_median": float(np.median(watts)), "socket_w_max": int(watts.max()),
             "gfx_clock_mhz_median_per_xcd": [int(v) for v in np.median(clocks, axis=0)]
             if len(clocks) else None,
-            "us_per_call_wall": round(elapsed / calls * 1e6, 1)}
+            "us_per_call_wall": round(us_per_call, 1)}
 
 
 def multiply_record(name, torch, bmm, steps):
@@ -633,7 +642,11 @@ def main():
     default_run = (w.name == workloads.HEADLINE and args.kernel == "auto" and not args.kmajor
                    and ka == 16 and splits is None and args.alpha is None and args.beta is None)
     if args.power or (default_run and not args.no_power):
-        line["power"] = power_sample(multiply, torch)
+        try:
+            line["power"] = power_sample(multiply, torch)
+        except Exception as e:   # telemetry only: never lose the line to it
+            log(f"[bench] power sample failed: {e!r}")
+            line["power"] = None
         log(f"[bench] power while the multiply runs: {line['power']}")
     if default_run and not args.no_extra:
         line["extra_records"] = {n: multiply_record(n, torch, bmm, args.steps)

@@ -126,6 +126,20 @@ def test_parse_amd_smi_metric():
     assert bench.parse_amd_smi_metric("command not found") == (None, [])
 
 
+def test_summarize_power_drops_unsettled_and_ragged_samples():
+    """Samples before the settle time are left out; a sample that lists fewer
+    XCD clocks than the others still counts for power but not for the clocks."""
+    samples = [(0.5, 900, [2400, 2400]), (1.2, 1398, [1800, 1900]), (1.6, 1400, [1820]),
+               (2.1, 1396, [1840, 1880]), (2.6, 1399, [])]
+    p = bench.summarize_power(samples, 1.0, 740.04)
+    assert p["samples"] == 4 and p["socket_w_max"] == 1400
+    assert p["socket_w_median"] == 1398.5
+    assert p["gfx_clock_mhz_median_per_xcd"] == [1820, 1890]
+    assert p["us_per_call_wall"] == 740.0
+    assert bench.summarize_power(samples[:1], 1.0, 740.0) is None
+    assert bench.summarize_power([(1.5, 1390, [])], 1.0, 1.0)["gfx_clock_mhz_median_per_xcd"] is None
+
+
 def test_extra_records_name_the_two_roofline_configs():
     """The extra records of the default run are the two other configurations
     with a roofline target: 4096^3 against the MFMA peak, the skinny shape
