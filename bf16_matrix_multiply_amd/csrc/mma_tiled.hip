@@ -443,20 +443,41 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     // ---- epilogue: one 16-byte store per block ----
+    // With alpha/beta and a C tensor, the C blocks of a group of kEpi blocks are
+    // all requested before the group's stores, so their reads overlap instead of
+    // waiting one by one. (D may be C: every element's C is read before its own
+    // D is written.)
+    constexpr int kEpi = kBM * kBN < 16 ? kBM * kBN : 16;
 #pragma unroll
-    for (int pm = 0; pm < kBM; ++pm)
+    for (int g0 = 0; g0 < kBM * kBN; g0 += kEpi) {
+      f32x4 cv[16];   // fixed size: used up to kEpi
 #pragma unroll
-      for (int qn = 0; qn < kBN; ++qn) {
+      for (int j = 0; j < kEpi; ++j) {
+        cv[j] = f32x4{p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
+        if constexpr (kScaled && kHasC) {
+          // no branch around the read (lanes past the edge read a clamped,
+          // in-bounds block and store nothing): a branch per read would make
+          // each read wait for the previous one
+          const int pm = (g0 + j) / kBN, qn = (g0 + j) % kBN;
+          const int64_t ra = lane_row_atom + pm, ca = lane_col_atom + 2 * qn;
+          const int64_t off =
+              interior ? d_lane + pm * d_mstride + 2 * qn * kAtomFloats
+                       : (((tc.b * p.M_rep + (ra < p.M_rep ? ra : p.M_rep - 1)) * p.N_rep +
+                           (ca < p.N_rep ? ca : p.N_rep - 1)) * 16 + (lane & 15)) * 8 +
+                             4 * (g16 & 1);
+          cv[j] = load16f_nt(p.C + off);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kEpi; ++j) {
+        const int pm = (g0 + j) / kBN, qn = (g0 + j) % kBN;
         f32x4 v = acc[pm][qn];
         float* dst = Dout + d_lane + pm * d_mstride + 2 * qn * kAtomFloats;
-        const bool ok = interior || (lane_row_atom + pm < p.M_rep && lane_col_atom + 2 * qn < p.N_rep);
+        const bool ok =
+            interior || (lane_row_atom + pm < p.M_rep && lane_col_atom + 2 * qn < p.N_rep);
         if constexpr (kScaled) {
-          f32x4 cv = {p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
-          if constexpr (kHasC) {
-            if (ok) cv = load16f_nt(p.C + (dst - Dout));
-          }
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.alpha, v[e], p.beta * cv[e]);
+          for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.alpha, v[e], p.beta * cv[j][e]);
         }
         if (ok) {
           if (p.splits > 1)
@@ -465,6 +486,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
             store16f_nt(dst, v);
         }
       }
+    }
   } else {
   // ---- accumulators: C (read once, here) or the scalar ----
     // Block (pm, qn) of the wave: rows 32 * (4 wm + pm) .. +31, columns
@@ -596,32 +618,46 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   
     // ---- epilogue: per block, four 16-byte stores (one per N atom) ----
+    // With alpha/beta and a C tensor, all of the wave's C reads are requested
+    // before its stores (D may be C: every element's C is read before its own D
+    // is written).
+    constexpr int kStores = kWaveBlocksM * kWaveBlocksN * 4;
+    static_assert(kStores <= 16, "one batch of C reads");
+    f32x4 cv[16];   // fixed size: used up to kStores
 #pragma unroll
-    for (int pm = 0; pm < kWaveBlocksM; ++pm)
+    for (int j = 0; j < kStores; ++j) {
+      cv[j] = f32x4{p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
+      if constexpr (kScaled && kHasC) {
+        // no branch around the read: lanes past the edge read a clamped block
+        const int pm = j / (4 * kWaveBlocksN), qn = (j / 4) % kWaveBlocksN, q = j % 4;
+        const int64_t ra = lane_row_atom + 2 * pm, ca = lane_col_atom + 4 * qn + q;
+        const int64_t off =
+            interior ? d_lane + 2 * pm * d_mstride + (4 * qn + q) * kAtomFloats
+                     : (((tc.b * p.M_rep + (ra < p.M_rep ? ra : p.M_rep - 1)) * p.N_rep +
+                         (ca < p.N_rep ? ca : p.N_rep - 1)) * 16 + (lane & 15)) * 8 +
+                           4 * (lane >> 5);
+        cv[j] = load16f_nt(p.C + off);
+      }
+    }
 #pragma unroll
-      for (int qn = 0; qn < kWaveBlocksN; ++qn)
+    for (int j = 0; j < kStores; ++j) {
+      const int pm = j / (4 * kWaveBlocksN), qn = (j / 4) % kWaveBlocksN, q = j % 4;
+      f32x4 v = {acc[pm][qn][4 * q + 0], acc[pm][qn][4 * q + 1], acc[pm][qn][4 * q + 2],
+                 acc[pm][qn][4 * q + 3]};
+      float* dst = Dout + d_lane + 2 * pm * d_mstride + (4 * qn + q) * kAtomFloats;
+      const bool ok =
+          interior || (lane_row_atom + 2 * pm < p.M_rep && lane_col_atom + 4 * qn + q < p.N_rep);
+      if constexpr (kScaled) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          f32x4 v = {acc[pm][qn][4 * q + 0], acc[pm][qn][4 * q + 1], acc[pm][qn][4 * q + 2],
-                     acc[pm][qn][4 * q + 3]};
-          float* dst = Dout + d_lane + 2 * pm * d_mstride + (4 * qn + q) * kAtomFloats;
-          const bool ok =
-              interior || (lane_row_atom + 2 * pm < p.M_rep && lane_col_atom + 4 * qn + q < p.N_rep);
-          if constexpr (kScaled) {
-            f32x4 cv = {p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
-            if constexpr (kHasC) {
-              if (ok) cv = load16f_nt(p.C + (dst - Dout));
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.alpha, v[e], p.beta * cv[e]);
-          }
-          if (ok) {
-            if (p.splits > 1)
-              store16f(dst, v);   // partial sums: read back by the reduce right away
-            else
-              store16f_nt(dst, v);
-          }
-        }
+        for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.alpha, v[e], p.beta * cv[j][e]);
+      }
+      if (ok) {
+        if (p.splits > 1)
+          store16f(dst, v);   // partial sums: read back by the reduce right away
+        else
+          store16f_nt(dst, v);
+      }
+    }
   }
 }
 
