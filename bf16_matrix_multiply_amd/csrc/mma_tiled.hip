@@ -7,10 +7,13 @@
 // Macro tiles (TM x TN of D) and their schedules:
 // - without split-K or alpha/beta, every tile: 4 waves in a 2 x 2 grid, each
 //   TM/2 x TN/2 of D (mma_tiled4_kernel), v_mfma_f32_16x16x32_{bf16,f16}; one
-//   workgroup per CU for 256 rows (one wave per SIMD), two for 128 x 128;
-// - with split-K or alpha/beta: 256 x 256 and 256 x 128 run 8 waves (two per
-//   SIMD) in two groups that alternate ("ping-pong", below), 16x16x32; 128 x
-//   128 runs 4 waves (two workgroups per CU), one group, v_mfma_f32_32x32x16.
+//   workgroup per CU for 256 rows (one wave per SIMD), two for 128 x 128; with
+//   alpha/beta the same pipeline for 256 x 128 and for 256 x 256 grids of more
+//   than one round (the product from zero, C read in the epilogue);
+// - with split-K, or alpha/beta on the other grids: 256 x 256 and 256 x 128 run
+//   8 waves (two per SIMD) in two groups that alternate ("ping-pong", below),
+//   16x16x32; 128 x 128 runs 4 waves (two workgroups per CU), one group,
+//   v_mfma_f32_32x32x16.
 // All of them give the same bits: each 32-deep step adds the same 32 products
 // per output to the same accumulator, in the same order of steps.
 //
@@ -61,7 +64,7 @@
 // run the same number of barriers. Each barrier is a bare s_barrier after a
 // counted wait, so loads of later slabs stay in flight across it.
 //
-// 4-wave tiles (no split-K, no alpha/beta): in the 256 x 256 tile a wave's 64
+// 4-wave tiles (no split-K): in the 256 x 256 tile a wave's 64
 // accumulators of 4 floats fill the 256 accumulator registers, so it holds a
 // 128 x 128 block and reads a third fewer LDS bytes per MFMA than a ping-pong
 // wave. A wave keeps the pipe fed by placing the next slab's fragment reads and
@@ -74,6 +77,10 @@
 // 52.9 us), where the ping-pong phases of 16 MFMAs per wave left the pipe half
 // idle; the 128 x 128 tile 5-9% faster than the one-group 32x32x16 schedule
 // (2048^3 23.0 against 25.3 us, 2048 x 2048 x 8192 69.5 against 74.4 us).
+// With alpha/beta the accumulators start from zero and the epilogue reads C in
+// batches of up to 16 blocks, with no branch around the reads, before the
+// batch's stores; the launch takes this pipeline only for the grids where it
+// measured faster (the launch code below lists them).
 //
 // The 128 x 128 tile with split-K or alpha/beta (two workgroups per CU, one
 // wave per SIMD each) keeps a one-group schedule: per slab, the MFMAs of the first 16-value half on
@@ -671,7 +678,7 @@ __attribute__((amdgpu_waves_per_eu(2))) void mma_tiled_kernel(MmaArgs p, int64_t
 // tiles). The next slab's fragments go to a second register set while the
 // current one is multiplied. 256-row tiles run one workgroup per CU (one wave
 // per SIMD); 128 x 128 tiles (64 KB of LDS) two.
-template <int TM, int TN, int DT, int KA, bool kHasC>
+template <int TM, int TN, int DT, int KA, bool kHasC, bool kScaled>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 256 ? 1 : 2, TM == 256 ? 1 : 2)))
 void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
   using T = Tile<TM, TN>;
@@ -746,7 +753,7 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
       (((tc.b * p.M_rep + lane_row_atom) * p.N_rep + lane_col_atom) * 16 + (lane & 15)) * 8 +
       4 * (g16 & 1);
   const int64_t d_mstride = p.N_rep * kAtomFloats;   // next M atom
-  if constexpr (kHasC) {
+  if constexpr (kHasC && !kScaled) {
     if (interior) {
       const float* cl = p.C + d_lane;
 #pragma unroll
@@ -772,8 +779,10 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
 #pragma unroll
       for (int qn = 0; qn < kBN; ++qn) {
         // Pinned to accumulator registers one by one: equal starting values
-        // would otherwise be merged, and the loop would then copy them.
-        f32x4 v = f32x4{p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
+        // would otherwise be merged, and the loop would then copy them. (The
+        // alpha/beta form starts the product from zero; C enters at the end.)
+        const float c0 = kScaled ? 0.f : p.c_scalar;
+        f32x4 v = f32x4{c0, c0, c0, c0};
         asm volatile("" : "+a"(v));
         acc[pm][qn] = v;
       }
@@ -847,14 +856,51 @@ void mma_tiled4_kernel(MmaArgs p, int64_t n_tiles, int64_t MT, int64_t NT) {
   // No load may still be writing LDS when the workgroup ends.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
+  if constexpr (!kScaled) {
 #pragma unroll
-  for (int pm = 0; pm < kBM; ++pm)
+    for (int pm = 0; pm < kBM; ++pm)
 #pragma unroll
-    for (int qn = 0; qn < kBN; ++qn) {
-      const bool ok =
-          interior || (lane_row_atom + pm < p.M_rep && lane_col_atom + 2 * qn < p.N_rep);
-      if (ok) store16f_nt(p.D + d_lane + pm * d_mstride + 2 * qn * kAtomFloats, acc[pm][qn]);
+      for (int qn = 0; qn < kBN; ++qn) {
+        const bool ok =
+            interior || (lane_row_atom + pm < p.M_rep && lane_col_atom + 2 * qn < p.N_rep);
+        if (ok) store16f_nt(p.D + d_lane + pm * d_mstride + 2 * qn * kAtomFloats, acc[pm][qn]);
+      }
+  } else {
+    // alpha/beta: D = fma(alpha, product, beta * C), one rounding after the
+    // product. The C blocks of a group of up to 16 are all requested, with no
+    // branch around the reads (lanes past the edge read a clamped block and
+    // store nothing), before the group's stores, so that the reads overlap.
+    // (D may be C: every element's C is read before its own D is written.)
+    constexpr int kEpi = kBM * kBN < 16 ? kBM * kBN : 16;
+#pragma unroll
+    for (int g0 = 0; g0 < kBM * kBN; g0 += kEpi) {
+      f32x4 cv[16];   // fixed size: used up to kEpi
+#pragma unroll
+      for (int j = 0; j < kEpi; ++j) {
+        cv[j] = f32x4{p.c_scalar, p.c_scalar, p.c_scalar, p.c_scalar};
+        if constexpr (kHasC) {
+          const int pm = (g0 + j) / kBN, qn = (g0 + j) % kBN;
+          const int64_t ra = lane_row_atom + pm, ca = lane_col_atom + 2 * qn;
+          const int64_t off =
+              interior ? d_lane + pm * d_mstride + 2 * qn * kAtomFloats
+                       : (((tc.b * p.M_rep + (ra < p.M_rep ? ra : p.M_rep - 1)) * p.N_rep +
+                           (ca < p.N_rep ? ca : p.N_rep - 1)) * 16 + (lane & 15)) * 8 +
+                             4 * (g16 & 1);
+          cv[j] = load16f_nt(p.C + off);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kEpi; ++j) {
+        const int pm = (g0 + j) / kBN, qn = (g0 + j) % kBN;
+        f32x4 v = acc[pm][qn];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __builtin_fmaf(p.alpha, v[e], p.beta * cv[j][e]);
+        const bool ok =
+            interior || (lane_row_atom + pm < p.M_rep && lane_col_atom + 2 * qn < p.N_rep);
+        if (ok) store16f_nt(p.D + d_lane + pm * d_mstride + 2 * qn * kAtomFloats, v);
+      }
     }
+  }
 }
 
 template <int TM, int TN>
@@ -882,10 +928,24 @@ hipError_t launch_tm(const MmaArgs& a, hipStream_t s) {
                                : pick_ka(std::integral_constant<int, kF16>{});
   const unsigned splits = a.splits > 1 ? unsigned(a.splits) : 1u;
   {
-    if (splits == 1 && !a.scaled) {
+    // The alpha/beta form takes the 4-wave pipeline where it measured faster
+    // than the ping-pong and one-group schedules (same bits): every 256 x 128
+    // grid (8192 x 1024 x 8192: 111.2 against 119.4 us; 2304 x 2304 x 4096: 49.8
+    // against 55.2) and 256 x 256 grids of more than one round of the chip's 256
+    // CUs (8192^3: 743.7 against 754.8). One round of 256 x 256 tiles (4096^3 with
+    // a C tensor: 94.2 against 92.2) and the 128 x 128 tile (2048^3: 24.3 against
+    // 23.6) keep the older schedules.
+    constexpr int64_t kOneRound = 256;
+    const bool four_wave =
+        !a.scaled || (TM == 256 && (TN == 128 || n_tiles > kOneRound));
+    if (splits == 1 && four_wave) {
       auto pick4 = [&](auto dt, auto ka) {
         constexpr int D = decltype(dt)::value, KA = decltype(ka)::value;
-        return a.C ? mma_tiled4_kernel<TM, TN, D, KA, true> : mma_tiled4_kernel<TM, TN, D, KA, false>;
+        if (a.scaled)
+          return a.C ? mma_tiled4_kernel<TM, TN, D, KA, true, true>
+                     : mma_tiled4_kernel<TM, TN, D, KA, false, true>;
+        return a.C ? mma_tiled4_kernel<TM, TN, D, KA, true, false>
+                   : mma_tiled4_kernel<TM, TN, D, KA, false, false>;
       };
       auto pick4_ka = [&](auto dt) {
         return a.atom_k == 16 ? pick4(dt, std::integral_constant<int, 16>{})

@@ -396,6 +396,29 @@ def test_scaled_in_place(kernel):
     assert np.array_equal(Cd.cpu().numpy(), ref)
 
 
+def test_scaled_multi_round_grids():
+    """The alpha/beta form on grids that take the 4-wave pipeline (256 x 128
+    tiles, and more than 256 tiles of 256 x 256) and on the others: 9 batches
+    of 1040 x 1288 x 80 (ragged in M, N and K; 270 tiles of 256 x 256, 495 of
+    256 x 128), quarter-integer data with C on the quarter grid and
+    power-of-two alpha, beta, so every kernel is bit-exact against the oracle's
+    alpha/beta form, in place (D = C) as well."""
+    w = C(9, 1040, 1288, 80, "bf16", "quarter", "quarter", c_tensor=True, name="scaled_rounds")
+    inp = inputs(w)
+    print(f"[scaled_rounds] {w.batch}x{w.M}x{w.N}x{w.K}", flush=True)
+    A = bmm.pack_operand(gu.dev_u16(inp["a"]), 16)
+    B = bmm.pack_operand(gu.dev_u16(inp["b"]), 8)
+    Ao, Bo = gu.oracle_operands(w, inp)
+    ref = oracle.mma_scaled(Ao, Bo, inp["c_tensor"], 0.0, 0.5, -2.0, w.dtype)
+    for kernel in ("tiled", "tiled256x128", "tiled128", "auto"):
+        Cd = torch.from_numpy(inp["c_tensor"]).cuda()
+        out = torch.full((w.batch, w.M_rep, w.N_rep, 16, 8), float("nan"), device="cuda")
+        D = bmm.mma_tile(A, B, Cd, 0.0, w.dtype, out=out, kernel=kernel, alpha=0.5, beta=-2.0)
+        assert np.array_equal(D.cpu().numpy(), ref), kernel
+        bmm.mma_tile(A, B, Cd, 0.0, w.dtype, out=Cd, kernel=kernel, alpha=0.5, beta=-2.0)
+        assert np.array_equal(Cd.cpu().numpy(), ref), kernel + " in place"
+
+
 def test_scaled_full_8192():
     """8192^3 bf16, C tensor, alpha=0.7, beta=-1.3: sampled outputs within
     1e-3 (|alpha||A||B|^T + |beta||C|) of alpha*P + beta*C, P the oracle's
